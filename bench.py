@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+Metric: paged decode KV-read GB/s (fraction of the 8 TB/s HBM peak) and
+microseconds per decode step; prefill TFLOP/s.
+
+One step = one pass of the decode hot path over the LLaMA-7B-shaped batch
+(8 sequences x 2048 tokens, 32/32 heads, head_dim 128, block_size 16, pool
+4096 blocks, fp16): the new token of every sequence is scattered into the
+pool through slot_mapping (paged_kv_write), then every sequence's query
+attends over its 2048 paged tokens (paged_attention_decode: split-KV
+partition pass + log-sum-exp reduce). Inputs are synthetic (N(0,1) values,
+a seeded random block permutation) and resident in HBM before timing. A
+>= 512 MiB buffer is rewritten between timed steps so that the 256 MB
+Infinity Cache does not serve the KV reads.
+
+Prints ONE JSON line. Extra fields carry the packed-prefill TFLOP/s, the
+ragged GQA and long-context decode figures, the roofline of the dominant
+kernel and the CPU oracle baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak, TFLOP/s
+FLUSH_BYTES = 1 << 30          # rewritten between timed steps (4x the Infinity Cache)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the decode step workload")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-step HIP events on the stream the library launches on."""
+
+    def __init__(self, torch, n):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are "
+                                   "not part of this build (use --gpus 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_39_amd import binding
+    from paged_kv_cache_39_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+    binding.lib()  # fail loudly before any timing if the library is missing
+
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def evict():
+        if flush is not None:
+            flush.bitwise_not_()
+
+    def tdt(dtype):
+        return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+    def ints(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def decode_setup(meta):
+        dt = tdt(meta.dtype)
+        shape = meta.pool_shape()
+        k = torch.randn(shape, dtype=dt, device=dev)
+        v = torch.randn(shape, dtype=dt, device=dev)
+        q = torch.randn(meta.num_seqs, meta.num_q_heads, meta.head_dim, dtype=dt, device=dev)
+        out = torch.empty_like(q)
+        bt, ctx = ints(meta.block_table), ints(meta.seq_lens)
+        ws_bytes = binding.paged_attention_decode_workspace_size(
+            meta.num_seqs, meta.num_q_heads, meta.head_dim, meta.max_blocks_per_seq,
+            meta.block_size)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        return dict(k=k, v=v, q=q, out=out, bt=bt, ctx=ctx, ws=ws)
+
+    def run_decode(meta, t):
+        binding.paged_attention_decode(t["out"], t["q"], t["k"], t["v"], t["bt"], t["ctx"],
+                                       meta.block_size, meta.scale, workspace=t["ws"])
+
+    # ------------------------------------------------------------------
+    # the step workload: LLaMA-7B-shaped decode, new token written + attended
+    # ------------------------------------------------------------------
+    meta = wl.workload(2, values=False)
+    t = decode_setup(meta)
+    dt = tdt(meta.dtype)
+    new_key = torch.randn(meta.num_seqs, meta.num_kv_heads, meta.head_dim, dtype=dt, device=dev)
+    new_val = torch.randn_like(new_key)
+    new_slots = ints(meta.slot_mapping[meta.new_token_rows])
+
+    def step():
+        binding.paged_kv_write(t["k"], t["v"], new_key, new_val, new_slots)
+        run_decode(meta, t)
+
+    for _ in range(args.warmup):
+        evict()
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, args.steps)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evict()
+        e0, e1, e2 = tm.ev[i]
+        e0.record()
+        binding.paged_kv_write(t["k"], t["v"], new_key, new_val, new_slots)
+        e1.record()
+        run_decode(meta, t)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(c) for a, b, c in tm.ev]
+    dec_ms = [b.elapsed_time(c) for a, b, c in tm.ev]
+    write_ms = [a.elapsed_time(b) for a, b, c in tm.ev]
+    ms_per_step = statistics.mean(step_ms)
+    e = wl.ELEM_BYTES[meta.dtype]
+    write_bytes = 2 * 2 * meta.num_seqs * meta.num_kv_heads * meta.head_dim * e + 4 * meta.num_seqs
+    step_bytes = meta.decode_bytes() + write_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_mean = statistics.mean(dec_ms)
+    dec_gbs = meta.decode_bytes() / (dec_mean * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode KV-read GB/s (% of HBM peak) + us/step; prefill TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: N(0,1) fp16 K/V/q, seeded random block permutation, inputs resident in HBM",
+        "config": {"workload": "llama7b-shaped paged decode step: write 1 new token/seq via "
+                               "slot_mapping, then decode", "batch": meta.num_seqs,
+                   "context": int(meta.seq_lens[0]), "q_heads": meta.num_q_heads,
+                   "kv_heads": meta.num_kv_heads, "head_dim": meta.head_dim,
+                   "block_size": meta.block_size, "pool_blocks": meta.num_blocks,
+                   "partition_tokens": binding.decode_partition_tokens(),
+                   "cache_flush_between_steps": flush is not None},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                                round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_call_us": round(dec_mean * 1e3, 2),
+        "decode_call_gbs": round(dec_gbs, 1),
+        "kv_write_call_us": round(statistics.mean(write_ms) * 1e3, 2),
+        "step_bytes": step_bytes,
+        "timed_wall_s": round(wall, 4),
+    }
+    result["roofline"] = {
+        "kernel": "paged_attention_decode (partition pass + reduce), LLaMA-7B-shaped batch",
+        "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        "algorithmic_bytes_per_launch": meta.decode_bytes(),
+    }
+    del t, new_key, new_val
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------
+    # other paths of the hot loop (same method: events per call, cache flush)
+    # ------------------------------------------------------------------
+    def time_calls(fn, n, warm=3):
+        for _ in range(warm):
+            evict()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            evict()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    if not args.no_extra:
+        n_extra = max(5, min(args.steps, 20))
+        extra = {}
+        for c in (3, 5):
+            m = wl.workload(c, values=False)
+            tt = decode_setup(m)
+            ms = time_calls(lambda: run_decode(m, tt), n_extra)
+            mu = statistics.mean(ms)
+            gbs = m.decode_bytes() / (mu * 1e-3) / 1e9
+            extra[m.name] = {"us": round(mu * 1e3, 2), "gbs": round(gbs, 1),
+                             "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "bytes": m.decode_bytes()}
+            del tt
+            torch.cuda.empty_cache()
+        m = wl.workload(4, values=False)
+        dtp = tdt(m.dtype)
+        k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
+        v = torch.randn_like(k)
+        q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp, device=dev)
+        out = torch.empty_like(q)
+        cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
+        ms = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
+                        n_extra)
+        mu = statistics.mean(ms)
+        fl = m.prefill_flops()
+        extra[m.name] = {"us": round(mu * 1e3, 2), "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
+                         "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "flops": fl, "total_q": int(m.cu_seqlens_q[-1])}
+        result["prefill_tflops"] = extra[m.name]["tflops"]
+        result["other_workloads"] = extra
+        del k, v, q, out
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on the host cores: one decode step of the
+    same LLaMA-7B-shaped batch (write the 8 new tokens, then attend) over a
+    sample of (sequence, head) pairs. Reported in the metric's unit."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_39_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    case = wl.workload(2)
+    rows = case.new_token_rows
+    old = np.ones(case.key.shape[0], dtype=bool)
+    old[rows] = False
+    slots_old = np.where(old, case.slot_mapping, -1).astype(np.int32)
+    k0, v0 = oracle.write_kv(case.empty_pool(), case.empty_pool(), case.key, case.value,
+                             slots_old, case.block_size)
+    # the whole batch: 8 sequences x 32 heads
+    pairs = [(b, h) for b in range(case.num_seqs) for h in range(case.num_q_heads)]
+    steps = 0
+    t0 = time.perf_counter()
+    while True:   # repeat whole steps until about 10 s of CPU work
+        k1, v1 = oracle.write_kv(k0, v0, case.key[rows], case.value[rows],
+                                 case.slot_mapping[rows], case.block_size)
+        oracle.decode(case.q, k1, v1, case.block_table, case.seq_lens, case.block_size,
+                      case.scale, case.dtype, pairs=pairs)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or steps >= 200:
+            break
+    kv_bytes = steps * sum(int(case.seq_lens[b]) for b, _ in pairs) * 2 * case.head_dim * 2
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full decode steps of the LLaMA-7B-shaped batch, each an oracle "
+                      f"KV write of the 8 new tokens then all {len(pairs)} (sequence, head) pairs "
+                      f"over 2048 tokens; {dt:.2f} s",
+            "us_per_step": round(dt / steps * 1e6, 1),
+            "seconds": round(dt, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache is a pool of fixed-size physical blocks shared by every
+ * sequence. A sequence reaches its tokens through a row of `block_table`
+ * (logical block -> physical block id) and a length. Token `pos` of
+ * sequence `b` lives at
+ *     slot = block_table[b, pos / block_size] * block_size + pos % block_size
+ * ("model-infer-kvcache" skill page, section 3.1, physical layout and
+ * logical mapping). New tokens are written by slot (`slot_mapping`, same
+ * page, section 3.3); attention reads them back through `block_table`.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller. The library
+ *    never frees, retains or allocates memory.
+ *  - All tensors are dense, row-major (C order), with no padding.
+ *  - Pool layout (k_cache and v_cache alike): [num_blocks, block_size,
+ *    num_kv_heads, head_dim]. Slot s is row s of the pool viewed as
+ *    [num_blocks * block_size, num_kv_heads * head_dim].
+ *  - Integer metadata (block_table, context_lens, seq_lens, slot_mapping,
+ *    cu_seqlens_q) is int32. The skill page's notes require an int32
+ *    block_table.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it and returns; it never synchronises the device.
+ *    Ordering between calls (write before read) is the stream's order.
+ *  - Return value: PKV_OK (0) on success, or a negative pkv_status. A
+ *    negative status means nothing was launched, except PKV_ERR_HIP, which
+ *    reports a failed launch. pkv_status_string() describes a status.
+ *  - Supported: head_dim in {64, 128}; block_size in {16, 32, 64, 128};
+ *    num_q_heads a positive multiple of num_kv_heads; num_blocks *
+ *    block_size <= INT32_MAX.
+ *  - Device-side contents are the caller's contract: block ids in
+ *    [0, num_blocks) for every block a sequence uses, context lengths
+ *    <= max_blocks_per_seq * block_size, cu_seqlens_q non-decreasing from 0
+ *    to total_q, slots unique. The kernels clamp what they read to the pool
+ *    and the table so that a violation never makes them access memory
+ *    outside the buffers, but the numerical result of such a call is
+ *    unspecified.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, out, key, value and the pool. */
+typedef enum {
+  PKV_F32 = 0,  /* IEEE binary32 */
+  PKV_F16 = 1,  /* IEEE binary16 */
+  PKV_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  PKV_ERR_DTYPE = -3,       /* dtype code unknown or not accepted by this call */
+  PKV_ERR_UNSUPPORTED = -4, /* head_dim / block_size outside the supported set */
+  PKV_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
+  PKV_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+} pkv_status;
+
+/*
+ * paged_kv_write -- scatter new K/V tokens into the pool by slot.
+ *
+ * For every t < num_tokens with s = slot_mapping[t] >= 0, copies key[t]
+ * into k_cache row s and value[t] into v_cache row s (all kv heads, all
+ * dims). A bit copy: no rounding, NaN payloads preserved. Tokens with a
+ * negative slot are skipped (a -1 entry marks "no slot"; the "Paged KV infra"
+ * page initialises unused table entries to -1). Slots >= num_blocks *
+ * block_size are skipped too. Duplicate slots race; which token lands is
+ * unspecified. Defined by the skill page, section 3.3 (slot_mapping drives
+ * the cache write) and section 3.1 (slot -> block, offset).
+ *
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   key, value       : [num_tokens, num_kv_heads, head_dim], dtype
+ *   slot_mapping     : [num_tokens] int32
+ *   num_tokens       : >= 0 (0 is a no-op that returns PKV_OK)
+ */
+int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
+                   const int32_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                   void* stream);
+
+/*
+ * paged_attention_decode_workspace_size -- bytes of device workspace that
+ * paged_attention_decode needs for these sizes (split-KV partial results:
+ * one (max, sum, unnormalised output) triple per sequence, query head and
+ * context partition, in fp32). Returns 0 for invalid sizes.
+ */
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq,
+                                             int32_t block_size);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends over its
+ * paged context.
+ *
+ * For sequence b and query head h (kv head h / (num_q_heads / num_kv_heads)):
+ *   out[b, h] = sum_j softmax_j(scale * <q[b, h], K_j>) * V_j
+ * over the context_lens[b] tokens j read through block_table[b]. A context
+ * length of 0 gives an all-zero output row. This is the decode setting of the
+ * skill page (Appendix C, sparse_mode 0: no mask, the KV length alone bounds
+ * the keys; section 3.6: the KV length includes the token just written), and
+ * the per-page attention of the "ATB PagedAttention" page. Long contexts are
+ * split into partitions whose partial softmax results are merged exactly
+ * (the vLLM-on-CANN page: scattered blocks are merged block by block with an
+ * online softmax).
+ *
+ *   out              : [num_seqs, num_q_heads, head_dim], dtype (written)
+ *   q                : [num_seqs, num_q_heads, head_dim], dtype
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   block_table      : [num_seqs, max_blocks_per_seq] int32
+ *   context_lens     : [num_seqs] int32, each in [0, max_blocks_per_seq*block_size]
+ *   scale            : softmax scale (1/sqrt(head_dim) in the pages' usage)
+ *   workspace        : device scratch of >= workspace_bytes bytes, where
+ *                      workspace_bytes >= paged_attention_decode_workspace_size(...)
+ *                      (may be NULL when that size is 0). Its contents on
+ *                      entry do not matter; it is clobbered. Two calls that
+ *                      share a workspace must be ordered on one stream.
+ * Accepts dtype PKV_F32, PKV_F16, PKV_BF16. Accumulation is fp32.
+ */
+int paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           int32_t block_size, float scale, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_varlen -- packed variable-length (prefill) attention over
+ * the paged cache.
+ *
+ * Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q and
+ * out, and keys/values 0 .. seq_lens[b]-1 read through block_table[b]
+ * (the packed layout of the "Paged KV infra" page, section 3.1: cu_seqlens
+ * has num_seqs+1 entries starting at 0, and each sequence gets its own
+ * causal mask over its own length, without padding). With causal != 0,
+ * local query i of a sequence with Lq queries and Lk keys sees keys
+ * j <= i + Lk - Lq (aligned to the last key, so that Lq == Lk is the usual
+ * lower-triangular mask and Lq == 1 is decode). A query row with no visible
+ * key outputs zeros. The softmax scale is 1/sqrt(head_dim) (the skill
+ * page's FA settings).
+ *
+ *   out              : [total_q, num_q_heads, head_dim], dtype (written)
+ *   q                : [total_q, num_q_heads, head_dim], dtype
+ *   cu_seqlens_q     : [num_seqs + 1] int32
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   block_table      : [num_seqs, max_blocks_per_seq] int32
+ *   seq_lens         : [num_seqs] int32 (KV length per sequence)
+ * Accepts dtype PKV_F16 and PKV_BF16 (matrix-core path); fp32 accumulation.
+ */
+int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int causal,
+                           int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                           void* stream);
+
+/* Static, human-readable text for a pkv_status value. Never NULL. */
+const char* pkv_status_string(int status);
+
+/* Tokens per split-KV partition used by paged_attention_decode. */
+int32_t pkv_decode_partition_tokens(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

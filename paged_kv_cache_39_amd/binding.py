@@ -1,0 +1,204 @@
+"""Thin Python binding of libpagedkv.so (argument marshalling only).
+
+Each function takes torch tensors that live on the GPU, checks dtype,
+device, contiguity and shape consistency, and passes raw device pointers and
+sizes to the C entry point of the same name (include/pagedkv.h), enqueued on
+torch's current stream. Every step of the computation runs in the HIP
+kernels; if the library is missing these functions raise instead of falling
+back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+_lib = None
+_lock = threading.Lock()
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+
+class PagedKVError(RuntimeError):
+    """A libpagedkv call returned a negative status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpagedkv.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_39_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.paged_kv_write.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
+        L.paged_kv_write.restype = ctypes.c_int
+        L.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.paged_attention_decode_workspace_size.restype = sz
+        L.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32,
+                                             i32, i32, i32, i64, i32, vp, sz, vp]
+        L.paged_attention_decode.restype = ctypes.c_int
+        L.paged_attention_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i64,
+                                             i32, i32, i32, i32, i32, i64, i32, vp]
+        L.paged_attention_varlen.restype = ctypes.c_int
+        L.pkv_status_string.argtypes = [ctypes.c_int]
+        L.pkv_status_string.restype = ctypes.c_char_p
+        L.pkv_decode_partition_tokens.argtypes = []
+        L.pkv_decode_partition_tokens.restype = i32
+        _lib = L
+        return L
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PagedKVError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_gpu(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _code(t):
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _pool_dims(k_cache, v_cache):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
+    nb, bs, hkv, d = k_cache.shape
+    return nb, bs, hkv, d
+
+
+def paged_kv_write(k_cache, v_cache, key, value, slot_mapping, stream=None):
+    """Copy key[t] / value[t] into pool row slot_mapping[t] (skipped if < 0)."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("key", key), ("value", value)):
+        _need_gpu(n, t)
+    _need_gpu("slot_mapping", slot_mapping, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, Hkv, D] matching the pool")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise TypeError("key/value dtype must match the pool")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping must be [num_tokens]")
+    _check("paged_kv_write", lib().paged_kv_write(
+        _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(slot_mapping),
+        key.shape[0], hkv, d, bs, nb, _code(k_cache), _stream(stream)))
+
+
+def paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                          block_size):
+    return int(lib().paged_attention_decode_workspace_size(
+        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size))
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes, device, stream):
+    key = (device.index, stream.cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, block_size,
+                           scale, workspace=None, stream=None):
+    """Single-token paged decode; writes out [B, Hq, D]."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    _need_gpu("block_table", block_table, torch.int32)
+    _need_gpu("context_lens", context_lens, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [num_seqs, Hq, D]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q/out dtype must match the pool")
+    bsz, hq, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_decode_workspace_size(bsz, hq, d, maxblk, bs) if bsz else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    elif need:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_decode", lib().paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+        bs, float(scale), bsz, hq, hkv, d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes,
+        _stream(s)))
+
+
+def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
+                           causal=True, stream=None):
+    """Packed variable-length prefill; writes out [total_q, Hq, D]."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _need_gpu(n, t, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [total_q, Hq, D]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q/out dtype must match the pool")
+    nseq = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (nseq + 1,) or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q must be [num_seqs+1], block_table [num_seqs, max_blocks]")
+    total_q, hq, _ = q.shape
+    _check("paged_attention_varlen", lib().paged_attention_varlen(
+        _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), 1 if causal else 0, nseq, total_q, hq, hkv, d, bs, block_table.shape[1],
+        nb, _code(q), _stream(stream)))
+
+
+def decode_partition_tokens() -> int:
+    return int(lib().pkv_decode_partition_tokens())

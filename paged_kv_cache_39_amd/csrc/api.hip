@@ -1,0 +1,169 @@
+// C-ABI entry points of libpagedkv.so: argument validation, workspace
+// layout and dispatch to the HIP launchers. Declared in include/pagedkv.h.
+//
+// Every check here runs before any HIP call, so an invalid call returns its
+// status without touching the device (and works on a machine with no GPU).
+
+#include <limits.h>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+bool valid_dtype(int32_t d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+int elem_bytes(int32_t d) { return d == PKV_F32 ? 4 : 2; }
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+bool supported_block_size(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+// Common pool checks; returns PKV_OK or the first failing status.
+int check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_blocks > (int64_t)INT32_MAX / block_size) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+int decode_num_parts(int32_t max_blocks_per_seq, int32_t block_size) {
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * block_size;
+  return (int)((max_ctx + pkv::kDecodePart - 1) / pkv::kDecodePart);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case PKV_ERR_DTYPE: return "dtype code unknown or not accepted by this call";
+    case PKV_ERR_UNSUPPORTED: return "head_dim or block_size outside the supported set";
+    case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case PKV_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t pkv_decode_partition_tokens(void) { return pkv::kDecodePart; }
+
+int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
+                   const int32_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                   void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !key || !value || !slot_mapping) return PKV_ERR_NULL;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  if (row_bytes > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_tokens > INT64_MAX / (row_bytes / 16)) return PKV_ERR_SHAPE;
+  hipError_t err = pkv::launch_kv_write(k_cache, v_cache, key, value, slot_mapping, num_tokens,
+                                        (int)row_bytes, num_blocks * block_size,
+                                        static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq,
+                                             int32_t block_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return 0;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return 0;
+  const int64_t parts = decode_num_parts(max_blocks_per_seq, block_size);
+  if (parts <= 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+  // [B, Hq, P, 2] (max, sum) followed by [B, Hq, P, D] partial outputs, fp32
+  return (size_t)(rows * 2 + rows * head_dim) * sizeof(float);
+}
+
+int paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           int32_t block_size, float scale, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                            max_blocks_per_seq, block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.dtype = dtype;
+  a.num_parts = decode_num_parts(max_blocks_per_seq, block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_parts;
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_o = workspace ? static_cast<float*>(workspace) + rows * 2 : nullptr;
+  hipError_t err = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int causal,
+                           int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                           void* stream) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (dtype == PKV_F32) return PKV_ERR_DTYPE;  // matrix-core path: 16-bit inputs only
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 128) return PKV_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (total_q > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
+    return PKV_ERR_NULL;
+
+  pkv::VarlenArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.causal = causal ? 1 : 0;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.dtype = dtype;
+  hipError_t err = pkv::launch_varlen(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

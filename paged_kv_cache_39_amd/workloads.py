@@ -145,9 +145,10 @@ def _token_slots(table, lens, block_size):
 
 def decode_case(seed, context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
                 dtype, num_blocks=None, spare=0.1, max_blocks=None, name="decode",
-                perm_blocks=None):
+                perm_blocks=None, values=True):
     """A decode workload: every context token written, then one query per
-    sequence. ``context_lens`` may be an int list or a callable(rng)."""
+    sequence. ``context_lens`` may be an int list or a callable(rng).
+    ``values=False`` stops after the metadata draws (q/key/value are None)."""
     rng = np.random.default_rng(seed)
     lens = context_lens(rng) if callable(context_lens) else list(context_lens)
     lens = [int(x) for x in lens]
@@ -157,10 +158,12 @@ def decode_case(seed, context_lens, num_q_heads, num_kv_heads, head_dim, block_s
     perm = rng.permutation(num_blocks) if perm_blocks is None else perm_blocks(rng, num_blocks)
     table = _assign_blocks(rng, lens, block_size, num_blocks, max_blocks, perm)
     bsz = len(lens)
-    q = normal(rng, (bsz, num_q_heads, head_dim), dtype)
     total = sum(lens)
-    key = normal(rng, (total, num_kv_heads, head_dim), dtype)
-    value = normal(rng, (total, num_kv_heads, head_dim), dtype)
+    q = key = value = None
+    if values:
+        q = normal(rng, (bsz, num_q_heads, head_dim), dtype)
+        key = normal(rng, (total, num_kv_heads, head_dim), dtype)
+        value = normal(rng, (total, num_kv_heads, head_dim), dtype)
     slots = _token_slots(table, lens, block_size)
     # the last token of each non-empty sequence is the one a decode step writes
     ends = np.cumsum(lens)
@@ -173,10 +176,11 @@ def decode_case(seed, context_lens, num_q_heads, num_kv_heads, head_dim, block_s
 
 
 def varlen_case(seed, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, block_size,
-                dtype, causal=True, spare=0.1, num_blocks=None, name="varlen"):
+                dtype, causal=True, spare=0.1, num_blocks=None, name="varlen", values=True):
     """A packed prefill workload: ``kv_lens[b]`` tokens of sequence b are
     written to the pool; its last ``q_lens[b]`` positions are the queries.
-    Either list may be a callable(rng) (kv_lens may then use q_lens)."""
+    Either list may be a callable(rng) (kv_lens may then use q_lens).
+    ``values=False`` stops after the metadata draws (q/key/value are None)."""
     rng = np.random.default_rng(seed)
     ql = q_lens(rng) if callable(q_lens) else list(q_lens)
     ql = [int(x) for x in ql]
@@ -188,10 +192,12 @@ def varlen_case(seed, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, bloc
     perm = rng.permutation(num_blocks)
     table = _assign_blocks(rng, kl, block_size, num_blocks, None, perm)
     total_q = sum(ql)
-    q = normal(rng, (total_q, num_q_heads, head_dim), dtype)
     total = sum(kl)
-    key = normal(rng, (total, num_kv_heads, head_dim), dtype)
-    value = normal(rng, (total, num_kv_heads, head_dim), dtype)
+    q = key = value = None
+    if values:
+        q = normal(rng, (total_q, num_q_heads, head_dim), dtype)
+        key = normal(rng, (total, num_kv_heads, head_dim), dtype)
+        value = normal(rng, (total, num_kv_heads, head_dim), dtype)
     slots = _token_slots(table, kl, block_size)
     cu = np.zeros(len(ql) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(ql)
@@ -221,24 +227,26 @@ WORKLOADS = {
 }
 
 
-def workload(c: int) -> PagedCase:
-    """Named workload ``c`` (1..5), seeded with 1000 + c."""
+def workload(c: int, values: bool = True) -> PagedCase:
+    """Named workload ``c`` (1..5), seeded with 1000 + c. ``values=False``
+    returns only the metadata (lengths, block table, slots)."""
     seed = 1000 + c
     if c == 1:
         return decode_case(seed, [37, 100], 4, 4, 64, 16, "f32", num_blocks=16,
-                           name="tiny_decode_fp32")
+                           name="tiny_decode_fp32", values=values)
     if c == 2:
         return decode_case(seed, [2048] * 8, 32, 32, 128, 16, "f16", num_blocks=4096,
-                           name="llama7b_decode_fp16_b8_ctx2048")
+                           name="llama7b_decode_fp16_b8_ctx2048", values=values)
     if c == 3:
         return decode_case(seed, lambda rng: rng.integers(50, 2001, size=32).tolist(),
                            32, 8, 128, 32, "bf16", spare=0.1,
-                           name="ragged_gqa_decode_bf16_b32")
+                           name="ragged_gqa_decode_bf16_b32", values=values)
     if c == 4:
         return varlen_case(seed, lambda rng: log_uniform_lengths(rng, 16, 64, 2048),
                            lambda rng, ql: ql, 32, 8, 128, 128, "bf16", causal=True,
-                           spare=0.1, name="packed_varlen_causal_prefill_bf16_16seq")
+                           spare=0.1, name="packed_varlen_causal_prefill_bf16_16seq",
+                           values=values)
     if c == 5:
         return decode_case(seed, [131072] * 4, 64, 8, 128, 128, "bf16", num_blocks=4096,
-                           name="long_ctx_splitkv_decode_bf16_b4_ctx131072")
+                           name="long_ctx_splitkv_decode_bf16_b4_ctx131072", values=values)
     raise ValueError(f"no workload {c}")

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/pagedkv.h declares, and rejects invalid arguments with the documented
+status before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_39_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE = 0, -1, -2, -3
+PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libpagedkv.so not built")
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("paged_kv_write", "paged_attention_decode", "paged_attention_varlen",
+                 "paged_attention_decode_workspace_size", "pkv_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in pagedkv.h but not exported"
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        s = binding.status_string(st)
+        assert s and s != "unknown status"
+    assert binding.status_string(-99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def write(L, **kw):
+    a = dict(k=FAKE, v=FAKE, key=FAKE, value=FAKE, slots=FAKE, n=4, hkv=2, d=128, bs=16, nb=8,
+             dtype=1)
+    a.update(kw)
+    return L.paged_kv_write(a["k"], a["v"], a["key"], a["value"], a["slots"], a["n"], a["hkv"],
+                            a["d"], a["bs"], a["nb"], a["dtype"], None)
+
+
+def test_write_validation(L):
+    assert write(L, dtype=7) == PKV_ERR_DTYPE
+    assert write(L, n=-1) == PKV_ERR_SHAPE
+    assert write(L, d=96) == PKV_ERR_UNSUPPORTED
+    assert write(L, bs=24) == PKV_ERR_UNSUPPORTED
+    assert write(L, hkv=0) == PKV_ERR_SHAPE
+    assert write(L, nb=2**31 // 16) == PKV_ERR_SHAPE      # num_blocks * block_size > INT32_MAX
+    assert write(L, k=None) == PKV_ERR_NULL
+    assert write(L, slots=None) == PKV_ERR_NULL
+    assert write(L, n=0, k=None) == PKV_OK                # empty write is a no-op
+
+
+def decode(L, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, bs=16, scale=0.1, b=2, hq=8,
+             hkv=2, d=128, maxblk=64, nb=256, dtype=2, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["ctx"], a["bs"],
+                                    a["scale"], a["b"], a["hq"], a["hkv"], a["d"], a["maxblk"],
+                                    a["nb"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(L):
+    assert decode(L, dtype=3) == PKV_ERR_DTYPE
+    assert decode(L, hq=6, hkv=4) == PKV_ERR_SHAPE            # Hq % Hkv != 0
+    assert decode(L, d=80) == PKV_ERR_UNSUPPORTED
+    assert decode(L, bs=8) == PKV_ERR_UNSUPPORTED
+    assert decode(L, maxblk=0) == PKV_ERR_SHAPE
+    assert decode(L, b=-1) == PKV_ERR_SHAPE
+    assert decode(L, q=None) == PKV_ERR_NULL
+    assert decode(L, bt=None) == PKV_ERR_NULL
+    need = L.paged_attention_decode_workspace_size(2, 8, 128, 64, 16)
+    assert need > 0
+    assert decode(L, ws=None) == PKV_ERR_WORKSPACE
+    assert decode(L, wsb=need - 1) == PKV_ERR_WORKSPACE
+    assert decode(L, b=0, q=None) == PKV_OK                    # empty batch
+
+
+def test_decode_workspace_size(L):
+    part = L.pkv_decode_partition_tokens()
+    assert part == 512
+    # one partition -> no workspace
+    assert L.paged_attention_decode_workspace_size(8, 32, 128, part // 16, 16) == 0
+    # 131072-token contexts with bs 128: 256 partitions of (max, sum) + D floats
+    got = L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128)
+    assert got == 4 * 64 * 256 * (2 + 128) * 4
+    assert L.paged_attention_decode_workspace_size(0, 64, 128, 1024, 128) == 0
+    assert L.paged_attention_decode_workspace_size(4, 64, 96, 1024, 128) == 0
+
+
+def varlen(L, **kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, causal=1, b=2, tq=100,
+             hq=8, hkv=2, d=128, bs=128, maxblk=4, nb=16, dtype=2)
+    a.update(kw)
+    return L.paged_attention_varlen(a["out"], a["q"], a["cu"], a["k"], a["v"], a["bt"], a["sl"],
+                                    a["causal"], a["b"], a["tq"], a["hq"], a["hkv"], a["d"],
+                                    a["bs"], a["maxblk"], a["nb"], a["dtype"], None)
+
+
+def test_varlen_validation(L):
+    assert varlen(L, dtype=0) == PKV_ERR_DTYPE                 # fp32 not on the matrix-core path
+    assert varlen(L, dtype=9) == PKV_ERR_DTYPE
+    assert varlen(L, hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert varlen(L, d=256) == PKV_ERR_UNSUPPORTED
+    assert varlen(L, bs=256) == PKV_ERR_UNSUPPORTED
+    assert varlen(L, hq=256, hkv=1) == PKV_ERR_UNSUPPORTED     # group larger than a tile
+    assert varlen(L, tq=-5) == PKV_ERR_SHAPE
+    assert varlen(L, cu=None) == PKV_ERR_NULL
+    assert varlen(L, sl=None) == PKV_ERR_NULL
+    assert varlen(L, tq=0, q=None) == PKV_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libpagedkv.so not built")
+    k = torch.zeros(4, 16, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        binding.paged_kv_write(k, k, torch.zeros(1, 2, 64, dtype=torch.float16),
+                               torch.zeros(1, 2, 64, dtype=torch.float16),
+                               torch.zeros(1, dtype=torch.int32))
