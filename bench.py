@@ -11,8 +11,8 @@ pool through slot_mapping (paged_kv_write), then every sequence's query
 attends over its 2048 paged tokens (paged_attention_decode: split-KV
 partition pass + log-sum-exp reduce). Inputs are synthetic (N(0,1) values,
 a seeded random block permutation) and resident in HBM before timing. A
->= 512 MiB buffer is rewritten between timed steps so that the 256 MB
-Infinity Cache does not serve the KV reads.
+1 GiB buffer is read between timed steps so that the 256 MB Infinity Cache
+does not serve the KV reads (a read, so that no dirty lines are left behind).
 
 Prints ONE JSON line. Extra fields carry the packed-prefill TFLOP/s, the
 ragged GQA and long-context decode figures, the roofline of the dominant
@@ -32,7 +32,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak, TFLOP/s
-FLUSH_BYTES = 1 << 30          # rewritten between timed steps (4x the Infinity Cache)
+FLUSH_BYTES = 1 << 30          # read between timed steps (4x the Infinity Cache)
 
 
 def parse():
@@ -73,11 +73,12 @@ def main():
     torch.manual_seed(0)
     binding.lib()  # fail loudly before any timing if the library is missing
 
-    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, dtype=torch.float32,
+                                                  device=dev)
 
     def evict():
         if flush is not None:
-            flush.bitwise_not_()
+            flush.sum()
 
     def tdt(dtype):
         return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
@@ -162,7 +163,9 @@ def main():
                    "context": int(meta.seq_lens[0]), "q_heads": meta.num_q_heads,
                    "kv_heads": meta.num_kv_heads, "head_dim": meta.head_dim,
                    "block_size": meta.block_size, "pool_blocks": meta.num_blocks,
-                   "partition_tokens": binding.decode_partition_tokens(),
+                   "partition_tokens": binding.decode_partition_tokens(
+                       meta.num_seqs, meta.num_q_heads, meta.num_kv_heads,
+                       meta.max_blocks_per_seq, meta.block_size, torch.float16),
                    "cache_flush_between_steps": flush is not None},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),

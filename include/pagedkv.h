@@ -90,9 +90,10 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
 
 /*
  * paged_attention_decode_workspace_size -- bytes of device workspace that
- * paged_attention_decode needs for these sizes (split-KV partial results:
+ * paged_attention_decode needs for these sizes: the split-KV partial results,
  * one (max, sum, unnormalised output) triple per sequence, query head and
- * context partition, in fp32). Returns 0 for invalid sizes.
+ * 512-token context partition, fp32. Returns 0 when no workspace is needed
+ * (contexts of at most one partition) and for invalid sizes.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq,
@@ -119,11 +120,11 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   block_table      : [num_seqs, max_blocks_per_seq] int32
  *   context_lens     : [num_seqs] int32, each in [0, max_blocks_per_seq*block_size]
  *   scale            : softmax scale (1/sqrt(head_dim) in the pages' usage)
- *   workspace        : device scratch of >= workspace_bytes bytes, where
+ *   workspace        : device scratch of workspace_bytes bytes, where
  *                      workspace_bytes >= paged_attention_decode_workspace_size(...)
  *                      (may be NULL when that size is 0). Its contents on
- *                      entry do not matter; it is clobbered. Two calls that
- *                      share a workspace must be ordered on one stream.
+ *                      entry do not matter; it is clobbered. Calls that share
+ *                      a workspace must be ordered on one stream.
  * Accepts dtype PKV_F32, PKV_F16, PKV_BF16. Accumulation is fp32.
  */
 int paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -167,8 +168,15 @@ int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q
 /* Static, human-readable text for a pkv_status value. Never NULL. */
 const char* pkv_status_string(int status);
 
-/* Tokens per split-KV partition used by paged_attention_decode. */
-int32_t pkv_decode_partition_tokens(void);
+/*
+ * Tokens per context partition that paged_attention_decode uses for these
+ * sizes (informative; 0 for invalid sizes). Contexts longer than one
+ * partition are split, and the partial softmax results of the pieces are
+ * merged by an exact log-sum-exp reduce.
+ */
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t dtype);
 
 #ifdef __cplusplus
 }

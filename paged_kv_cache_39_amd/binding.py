@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_varlen.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
-        L.pkv_decode_partition_tokens.argtypes = []
+        L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pkv_decode_partition_tokens.restype = i32
         _lib = L
         return L
@@ -200,5 +200,9 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
         nb, _code(q), _stream(stream)))
 
 
-def decode_partition_tokens() -> int:
-    return int(lib().pkv_decode_partition_tokens())
+def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                            dtype=torch.float16) -> int:
+    """Context partition length paged_attention_decode uses for these sizes."""
+    return int(lib().pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
+                                                 max_blocks_per_seq, block_size,
+                                                 _DTYPE_CODE[dtype]))

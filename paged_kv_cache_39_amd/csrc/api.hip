@@ -6,7 +6,7 @@
 
 #include <limits.h>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "pkv_launch.h"
 
 namespace {
@@ -25,8 +25,8 @@ int check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64
 }
 
 int decode_num_parts(int32_t max_blocks_per_seq, int32_t block_size) {
-  const int64_t max_ctx = (int64_t)max_blocks_per_seq * block_size;
-  return (int)((max_ctx + pkv::kDecodePart - 1) / pkv::kDecodePart);
+  // the finest split any launch plan uses
+  return pkv::decode_parts(max_blocks_per_seq, block_size, pkv::kDecodePart);
 }
 
 }  // namespace
@@ -46,7 +46,19 @@ const char* pkv_status_string(int status) {
   }
 }
 
-int32_t pkv_decode_partition_tokens(void) { return pkv::kDecodePart; }
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq, int32_t block_size, int32_t dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !supported_block_size(block_size))
+    return 0;
+  if (dtype == PKV_F32) return pkv::kDecodePart;
+  const int group = num_q_heads / num_kv_heads;
+  int hpw = 1;
+  for (int c = 16; c >= 1; --c)
+    if (group % c == 0) { hpw = c; break; }
+  return pkv::plan_decode(num_seqs, num_q_heads / hpw, max_blocks_per_seq, block_size)
+      .part_tokens;
+}
 
 int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
                    const int32_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
@@ -67,6 +79,8 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// Workspace layout: [B, Hq, P, 2] fp32 (max, sum), then [B, Hq, P, D] fp32
+// partial outputs, P = partitions at the finest split.
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq,
                                              int32_t block_size) {
@@ -75,7 +89,6 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
   const int64_t parts = decode_num_parts(max_blocks_per_seq, block_size);
   if (parts <= 1) return 0;
   const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
-  // [B, Hq, P, 2] (max, sum) followed by [B, Hq, P, D] partial outputs, fp32
   return (size_t)(rows * 2 + rows * head_dim) * sizeof(float);
 }
 
@@ -114,10 +127,11 @@ int paged_attention_decode(void* out, const void* q, const void* k_cache, const 
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  a.num_parts = decode_num_parts(max_blocks_per_seq, block_size);
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_parts;
+  // partials are laid out for the finest split; a coarser launch plan uses a prefix
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
+                                                                          block_size);
   a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? static_cast<float*>(workspace) + rows * 2 : nullptr;
+  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   hipError_t err = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -28,6 +28,7 @@ namespace pkv {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kMaxPartTokens = 2048;   // longest partition a workgroup takes
 constexpr int kQuadsPerIter = 8;                  // each row handles 8 tokens per iteration
 constexpr int kTokPerIter = 4 * kQuadsPerIter;    // 32 tokens per wave iteration
 
@@ -93,8 +94,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
   const int lane_off = kvh * D + c * EPL;
   const int nchunks = (ntok + kTokPerIter - 1) / kTokPerIter;
   const int last_quad = (ntok - 1) & ~3;
-  const size_t part_base = (size_t)part_start;  // block aligned: kDecodePart % bs == 0
-  (void)part_base;
 
   for (int ci = wave; ci < nchunks; ci += kDecWaves) {
     Chunk<Ty, EPL> kr[kQuadsPerIter], vr[kQuadsPerIter];
@@ -110,8 +109,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
       const typename Ty::storage* kb = k_cache + (size_t)blk * bs * row_stride;
       const typename Ty::storage* vb = v_cache + (size_t)blk * bs * row_stride;
       const int off = (tok & (bs - 1)) * row_stride + lane_off;
-      kr[u] = load_chunk<Ty, EPL>(kb + off);
-      vr[u] = load_chunk<Ty, EPL>(vb + off);
+      kr[u] = load_chunk<Ty, EPL, true>(kb + off);
+      vr[u] = load_chunk<Ty, EPL, true>(vb + off);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -199,74 +198,382 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
   }
 }
 
-// Exact merge of the partition triples of one (sequence, query head):
-// M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
-template <class Ty, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(
-    typename Ty::storage* __restrict__ out, const float* __restrict__ ws_ml,
-    const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens, int num_q_heads,
-    int log2_bs, int max_blocks_per_seq, int num_parts) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// ---------------------------------------------------------------------------
+// Matrix-core decode (fp16 / bf16). One workgroup per (partition, group of up
+// to 16 query heads sharing a kv head, sequence); each of its WAVES waves owns
+// a contiguous share of the partition and walks it TT tokens at a time.
+//
+// K and V rows are fetched exactly as in the vector kernel (16 lanes x 16 B
+// per 256-byte row, non-temporal) into registers, one tile ahead, and parked
+// in a wave-private LDS tile. From there
+//   S^T = K Q^T     (A: K rows, ds_read_b128; B: the group's queries, held in
+//                    registers, heads padded to 16 with zeros; k = 32 MFMA)
+//   O^T += V^T P^T  (A: V^T via the LDS transpose read; B: P^T straight from
+//                    the S^T accumulators, rounded to the input type)
+// so each lane owns one query head's statistics and output rows; the token
+// max needs two cross-lane exchanges per tile and nothing else moves. The
+// waves are merged through LDS at the end.
+// ---------------------------------------------------------------------------
+
+template <int D, int WAVES, int TT>
+struct MfLds {
+  static constexpr int rowB = D * 2 + 16;            // padded row pitch (bytes)
+  static constexpr int tileB = TT * rowB;             // one K or V tile
+  static constexpr int waveB = 2 * tileB;
+  static constexpr int totalB = WAVES * waveB;
+  static constexpr int mergeB = WAVES * 16 * (D + 2) * 4;
+  static constexpr int bytes = totalB > mergeB ? totalB : mergeB;
+};
+
+template <class Ty, int D, int WAVES, int TT>
+__global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, float scale_log2, int num_q_heads,
+    int num_kv_heads, int group, int heads_per_wg, int log2_bs, int max_blocks_per_seq,
+    int64_t num_blocks, int num_parts, int part_tokens) {
+  using L = MfLds<D, WAVES, TT>;
+  constexpr int NT = WAVES * kWave;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;    // rows per load instruction
+  constexpr int LPI = TT / RPI;       // load instructions per tile
+  constexpr int KS = D / 32;          // k-steps of q.k
+  constexpr int ND = D / 16;          // 16-dim tiles of the output
+  constexpr int NS = TT / 16;         // 16-token blocks per tile
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_mem[L::bytes];
+  __shared__ int s_blk[kMaxPartTokens / 16];
+
+  const int p = blockIdx.x;
+  const int h0 = blockIdx.y * heads_per_wg;
+  const int kvh = h0 / group;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int lrow = lane / CPR, lch = lane % CPR;
+  const int bs = 1 << log2_bs;
+
   int ctx = context_lens[b];
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
-  const int np = (ctx + kDecodePart - 1) / kDecodePart;
+  const int part_start = p * part_tokens;
+  if (part_start >= ctx) {
+    if (p == 0) {
+      for (int i = tid; i < heads_per_wg * D; i += NT)
+        out[((size_t)b * num_q_heads + h0 + i / D) * D + i % D] = 0;
+    }
+    return;
+  }
+  const int ntok = min(part_tokens, ctx - part_start);
+  const int nparts_b = (ctx + part_tokens - 1) / part_tokens;
+
+  const int nblk = (ntok + bs - 1) >> log2_bs;
+  for (int i = tid; i < nblk; i += NT) {
+    const int id = block_table[(size_t)b * max_blocks_per_seq + (part_start >> log2_bs) + i];
+    s_blk[i] = (id >= 0 && id < num_blocks) ? id : -1;
+  }
+
+  // queries as the B operand: lane holds head h0 + l16, dims 32s + 8*g4 .. +8
+  const bool head_ok = l16 < heads_per_wg;
+  u32x4_t qb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qb[s] = head_ok ? load16<false>(q + ((size_t)b * num_q_heads + h0 + l16) * D + 32 * s + 8 * g4)
+                    : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  const int row_stride = num_kv_heads * D;
+  const int head_off = kvh * D + lch * 8;
+  // waves own contiguous, TT-aligned shares of the partition
+  const int share = ((ntok + WAVES * TT - 1) / (WAVES * TT)) * TT;
+  const int wtok0 = wave * share;
+  const int wtok_n = max(0, min(ntok - wtok0, share));
+  const int niter = (wtok_n + TT - 1) / TT;
+  const int last_grp = (ntok - 1) & ~(RPI - 1);
+
+  uint8_t* s_k = s_mem + wave * L::waveB;
+  uint8_t* s_v = s_k + L::tileB;
+
+  u32x4_t kr[LPI], vr[LPI];
+  auto fetch = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) {
+      const int t0 = wtok0 + it * TT + j * RPI;           // first row of this load (uniform)
+      const int tg = min(t0, last_grp);                    // groups past the end re-read the last
+      const int tok = min(tg + lrow, ntok - 1);
+      const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
+      const size_t off = ((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off;
+      kr[j] = load16<true>(k_cache + off);
+      vr[j] = load16<true>(v_cache + off);
+    }
+  };
+
+  f32x4_t acc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) acc[nd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // V^T operand: lane i of a 16-lane group points at token 4*g4 + i/4 (+16n),
+  // dims 16nd + 4*(i%4) .. +4, and receives dim 16nd + i of tokens 4*g4 .. +4
+  const uint8_t* vt = s_v + (4 * g4 + (l16 >> 2)) * L::rowB + (l16 & 3) * 8;
+
+  if (niter > 0) fetch(0);
+  for (int it = 0; it < niter; ++it) {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) {
+      *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 16) = kr[j];
+      *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 16) = vr[j];
+    }
+    if (it + 1 < niter) fetch(it + 1);
+
+    f32x4_t st[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      st[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(s_k + (16 * n + l16) * L::rowB + 64 * s + 16 * g4);
+        st[n] = Mma<Ty>::mfma(a, qb[s], st[n]);
+      }
+    }
+    // lane holds tokens 16n + 4*g4 + i of this tile for head l16
+    const int tbase = wtok0 + it * TT + 4 * g4;
+    float sv[NS][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[n][i] = (tbase + 16 * n + i < ntok) ? st[n][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[n][i]);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mnew = fmaxf(m_run, mx);
+    const float mref = safe_max_ref(mnew);
+    const float alpha = fast_exp2(m_run - mref);
+    m_run = mnew;
+    float pv[NS][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[n][i] = fast_exp2(sv[n][i] - mref);
+        psum += pv[n][i];
+      }
+    l_run = l_run * alpha + psum;
+    if constexpr (NS == 1) {
+      const u32x2_t pb = {Mma<Ty>::pack(pv[0][0], pv[0][1]), Mma<Ty>::pack(pv[0][2], pv[0][3])};
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const u32x2_t a = lds_read_tr16(vt + nd * 32);
+        acc[nd] *= alpha;
+        acc[nd] = Mma<Ty>::mfma16(a, pb, acc[nd]);
+      }
+    } else {
+      const u32x4_t pb = {Mma<Ty>::pack(pv[0][0], pv[0][1]), Mma<Ty>::pack(pv[0][2], pv[0][3]),
+                          Mma<Ty>::pack(pv[1][0], pv[1][1]), Mma<Ty>::pack(pv[1][2], pv[1][3])};
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const u32x2_t lo = lds_read_tr16(vt + nd * 32);
+        const u32x2_t hi = lds_read_tr16(vt + 16 * L::rowB + nd * 32);
+        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+        acc[nd] *= alpha;
+        acc[nd] = Mma<Ty>::mfma(a, pb, acc[nd]);
+      }
+    }
+  }
+
+  // ---- merge lanes (the 4 lane groups) and waves ----
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  __syncthreads();  // every wave is done with its K/V tiles
+  float* s_ml = reinterpret_cast<float*>(s_mem);                 // [wave][16][2]
+  float* s_o = s_ml + WAVES * 16 * 2;                            // [wave][16][D]
+  if (g4 == 0) {
+    s_ml[(wave * 16 + l16) * 2 + 0] = m_run;
+    s_ml[(wave * 16 + l16) * 2 + 1] = l_run;
+  }
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[(wave * 16 + l16) * D + 16 * nd + 4 * g4 + i] = acc[nd][i];
+  __syncthreads();
+
+  for (int idx = tid; idx < heads_per_wg * D; idx += NT) {
+    const int hh = idx / D, d = idx % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) mm = fmaxf(mm, s_ml[(w * 16 + hh) * 2]);
+    const float mr = safe_max_ref(mm);
+    float ll = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float wt = fast_exp2(s_ml[(w * 16 + hh) * 2] - mr);
+      ll += s_ml[(w * 16 + hh) * 2 + 1] * wt;
+      a += s_o[(w * 16 + hh) * D + d] * wt;
+    }
+    const size_t bh = (size_t)b * num_q_heads + h0 + hh;
+    if (nparts_b == 1) {
+      out[bh * D + d] = from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
+    } else {
+      ws_o[(bh * num_parts + p) * D + d] = a;
+      if (d == 0) {
+        ws_ml[(bh * num_parts + p) * 2 + 0] = mm;
+        ws_ml[(bh * num_parts + p) * 2 + 1] = ll;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact merge of the partition triples of one (sequence, query head):
+//   M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
+// 4 waves split the partitions; each lane owns D/64 output elements.
+// ---------------------------------------------------------------------------
+template <class Ty, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_reduce_kernel(
+    typename Ty::storage* __restrict__ out, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens, int num_q_heads,
+    int log2_bs, int max_blocks_per_seq, int num_parts, int part_tokens) {
+  constexpr int EPL = D / kWave;
+  __shared__ float s_red[kDecWaves];
+  __shared__ float s_acc[kDecWaves][D + 1];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ctx = context_lens[b];
+  ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
+  const int np = (ctx + part_tokens - 1) / part_tokens;
   if (np <= 1) return;
   const size_t bh = (size_t)b * num_q_heads + h;
   const float* ml = ws_ml + bh * num_parts * 2;
   const float* o = ws_o + bh * num_parts * D;
+
   float mm = -INFINITY;
-  for (int p = 0; p < np; ++p) mm = fmaxf(mm, ml[2 * p]);
+  for (int p = tid; p < np; p += kDecThreads) mm = fmaxf(mm, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
+  if (lane == 0) s_red[wave] = mm;
+  __syncthreads();
+  mm = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float mr = safe_max_ref(mm);
-  float ll = 0.f, acc = 0.f;
-  for (int p = 0; p < np; ++p) {
+
+  float a[EPL], ll = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = 0.f;
+  int p = wave;
+  for (; p + 3 * kDecWaves < np; p += 4 * kDecWaves) {
+    float w4[4], v4[4][EPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pp = p + u * kDecWaves;
+      w4[u] = fast_exp2(ml[2 * pp] - mr);
+      ll += ml[2 * pp + 1] * w4[u];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v4[u][e] = o[(size_t)pp * D + lane * EPL + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] += v4[u][e] * w4[u];
+  }
+  for (; p < np; p += kDecWaves) {
     const float wt = fast_exp2(ml[2 * p] - mr);
     ll += ml[2 * p + 1] * wt;
-    acc += o[(size_t)p * D + d] * wt;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] += o[(size_t)p * D + lane * EPL + e] * wt;
   }
-  out[bh * D + d] = from_f32<Ty>(ll > 0.f ? acc / ll : 0.f);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = ll;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_acc[wave][lane * EPL + e] = a[e];
+  __syncthreads();
+  if (tid < D) {
+    const float lt = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const float at = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
+    out[bh * D + tid] = from_f32<Ty>(lt > 0.f ? at / lt : 0.f);
+  }
+}
+
+template <class Ty, int D>
+static hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream, int log2_bs,
+                                int num_parts, int part_tokens) {
+  using S = typename Ty::storage;
+  hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(a.num_q_heads, a.num_seqs),
+                     dim3(kDecThreads), 0, stream, static_cast<S*>(a.out), a.ws_ml, a.ws_o,
+                     a.context_lens, a.num_q_heads, log2_bs, a.max_blocks_per_seq, num_parts,
+                     part_tokens);
+  return hipGetLastError();
 }
 
 template <class Ty, int D, int G>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   using S = typename Ty::storage;
   const int log2_bs = __builtin_ctz(a.block_size);
   const float scale_log2 = a.scale * 1.4426950408889634f;
   const int group = a.num_q_heads / a.num_kv_heads;
-  dim3 grid(a.num_parts, a.num_q_heads / G, a.num_seqs);
+  const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, kDecodePart);
+  dim3 grid(parts, a.num_q_heads / G, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<Ty, D, G>), grid, dim3(kDecThreads), 0, stream,
                      static_cast<S*>(a.out), static_cast<const S*>(a.q),
                      static_cast<const S*>(a.k_cache), static_cast<const S*>(a.v_cache),
                      a.block_table, a.context_lens, a.ws_ml, a.ws_o, scale_log2, a.num_q_heads,
-                     a.num_kv_heads, group, log2_bs, a.max_blocks_per_seq, a.num_blocks,
-                     a.num_parts);
+                     a.num_kv_heads, group, log2_bs, a.max_blocks_per_seq, a.num_blocks, parts);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.num_parts <= 1) return err;
-  hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0,
-                     stream, static_cast<S*>(a.out), a.ws_ml, a.ws_o, a.context_lens,
-                     a.num_q_heads, log2_bs, a.max_blocks_per_seq, a.num_parts);
-  return hipGetLastError();
+  if (err != hipSuccess || parts <= 1) return err;
+  return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
+}
+
+template <class Ty, int D, int WAVES, int TT>
+static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
+                                  int part_tokens) {
+  const int log2_bs = __builtin_ctz(a.block_size);
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
+  dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT>), grid, dim3(WAVES * kWave), 0, stream,
+                     static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k_cache),
+                     static_cast<const uint16_t*>(a.v_cache), a.block_table, a.context_lens,
+                     a.ws_ml, a.ws_o, scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw,
+                     log2_bs, a.max_blocks_per_seq, a.num_blocks, parts, part_tokens);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || parts <= 1) return err;
+  return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
 }
 
 template <class Ty, int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
-  const int g = a.num_q_heads / a.num_kv_heads;
-  if (g % 8 == 0) return launch_decode_t<Ty, D, 8>(a, stream);
-  if (g % 4 == 0) return launch_decode_t<Ty, D, 4>(a, stream);
-  if (g % 2 == 0) return launch_decode_t<Ty, D, 2>(a, stream);
-  return launch_decode_t<Ty, D, 1>(a, stream);
+static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  int hpw = 1;  // largest divisor of the group size that fits one 16-row tile
+  for (int c = 16; c >= 1; --c)
+    if (group % c == 0) { hpw = c; break; }
+  const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
+                                      a.block_size);
+  if (plan.waves == 8) return launch_mfma_cfg<Ty, D, 8, 32>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16>(a, stream, hpw, plan.part_tokens);
 }
 
-template <class Ty>
-static hipError_t launch_decode_ty(const DecodeArgs& a, hipStream_t stream) {
-  if (a.head_dim == 64) return launch_decode_d<Ty, 64>(a, stream);
-  return launch_decode_d<Ty, 128>(a, stream);
+template <int D>
+static hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  if (g % 8 == 0) return launch_decode_valu<F32, D, 8>(a, stream);
+  if (g % 4 == 0) return launch_decode_valu<F32, D, 4>(a, stream);
+  if (g % 2 == 0) return launch_decode_valu<F32, D, 2>(a, stream);
+  return launch_decode_valu<F32, D, 1>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_dim == 64;
   switch (a.dtype) {
-    case 0: return launch_decode_ty<F32>(a, stream);
-    case 1: return launch_decode_ty<F16>(a, stream);
-    default: return launch_decode_ty<BF16>(a, stream);
+    case 0: return d64 ? launch_decode_f32<64>(a, stream) : launch_decode_f32<128>(a, stream);
+    case 1: return d64 ? launch_decode_mfma<F16, 64>(a, stream)
+                       : launch_decode_mfma<F16, 128>(a, stream);
+    default: return d64 ? launch_decode_mfma<BF16, 64>(a, stream)
+                        : launch_decode_mfma<BF16, 128>(a, stream);
   }
 }
 

@@ -8,6 +8,24 @@ namespace pkv {
 
 constexpr int kWave = 64;
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global load, optionally non-temporal
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+
 // ---------------------------------------------------------------------------
 // element types: storage form and exact widening to fp32
 // ---------------------------------------------------------------------------
@@ -71,8 +89,10 @@ struct Chunk<F32, EPL> {
 };
 
 // Load one lane's chunk (EPL consecutive elements) with 16-byte / 8-byte
-// vector loads. `p` must be aligned to the chunk size.
-template <class Ty, int EPL>
+// vector loads. `p` must be aligned to the chunk size. NT marks the load
+// non-temporal: data streamed once (the KV pool) then does not displace
+// reusable lines, and it is not slowed down by dirty lines in the caches.
+template <class Ty, int EPL, bool NT = false>
 __device__ __forceinline__ Chunk<Ty, EPL> load_chunk(const typename Ty::storage* p) {
   Chunk<Ty, EPL> c;
   constexpr int words = sizeof(c.w) / 4;
@@ -80,12 +100,13 @@ __device__ __forceinline__ Chunk<Ty, EPL> load_chunk(const typename Ty::storage*
   if constexpr (words % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < words; i += 4) {
-      uint4 v = *reinterpret_cast<const uint4*>(src + i);
-      c.w[i] = v.x; c.w[i + 1] = v.y; c.w[i + 2] = v.z; c.w[i + 3] = v.w;
+      const u32x4_t v = load16<NT>(src + i);
+      c.w[i] = v[0]; c.w[i + 1] = v[1]; c.w[i + 2] = v[2]; c.w[i + 3] = v[3];
     }
   } else if constexpr (words == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(src);
-    c.w[0] = v.x; c.w[1] = v.y;
+    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(src);
+    const u32x2_t v = NT ? __builtin_nontemporal_load(q) : *q;
+    c.w[0] = v[0]; c.w[1] = v[1];
   } else {
 #pragma unroll
     for (int i = 0; i < words; ++i) c.w[i] = src[i];
@@ -152,5 +173,58 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Merge weight for a partial with running max m against the merged max
 // `mref`, where mref == -inf means "nothing seen yet" (weight 0 for m=-inf).
 __device__ __forceinline__ float safe_max_ref(float m) { return m == -INFINITY ? 0.f : m; }
+
+// ---------------------------------------------------------------------------
+// matrix cores: v_mfma_f32_16x16x32_{bf16,f16} (mfma) and the k = 16 forms
+// v_mfma_f32_16x16x16{bf16_1k,f16} (mfma16)
+//   A (16 x K): lane l holds row l%16, k = (K/4)*(l/16) .. +K/4
+//   B (K x 16): lane l holds column l%16, k = (K/4)*(l/16) .. +K/4
+//   D (16 x 16): lane l, register i holds row 4*(l/16) + i, column l%16
+// ---------------------------------------------------------------------------
+
+template <class Ty>
+struct Mma;
+template <>
+struct Mma<BF16> {
+  static __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // k = 16 variant: lane l holds k = 4*(l/16) .. +4 of its row / column
+  static __device__ __forceinline__ f32x4_t mfma16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair, round to nearest even
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+template <>
+struct Mma<F16> {
+  static __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i supplies the address of a row R_i of four 16-bit elements; lane
+// 4a+b receives (R_a[b], R_{a+4}[b], R_{a+8}[b], R_{a+12}[b]).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+  return __builtin_bit_cast(u32x2_t, v);
+}
 
 }  // namespace pkv

@@ -9,8 +9,36 @@
 
 namespace pkv {
 
-// Tokens per split-KV partition of the decode path.
+// Tokens per split-KV partition of the decode path (the long-context split),
+// and the longest single partition a decode workgroup takes when the batch
+// alone already fills the chip.
 constexpr int kDecodePart = 512;
+constexpr int kDecodeWidePart = 2048;
+constexpr int kNumCUs = 256;
+
+inline int decode_parts(int max_blocks_per_seq, int block_size, int part_tokens) {
+  const long long max_ctx = (long long)max_blocks_per_seq * block_size;
+  return (int)((max_ctx + part_tokens - 1) / part_tokens);
+}
+
+// Launch plan of the matrix-core decode: `rows` = sequences x head groups.
+// With at least one row per compute unit and contexts up to 2048 tokens, one
+// 8-wave workgroup takes a whole context (no split, no reduce); otherwise the
+// context is split into 512-token partitions for 4-wave workgroups and the
+// partial results are merged by the reduce kernel.
+struct DecodePlan {
+  int waves;
+  int part_tokens;
+};
+inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size) {
+  const long long rows = (long long)num_seqs * groups;
+  const long long max_ctx = (long long)max_blocks_per_seq * block_size;
+  if (rows >= kNumCUs && max_ctx <= kDecodeWidePart) {
+    const int part = (int)((max_ctx + kDecodePart - 1) / kDecodePart * kDecodePart);
+    return {8, part};
+  }
+  return {4, kDecodePart};
+}
 
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
                            const int32_t* slot_mapping, int64_t num_tokens, int row_bytes,
@@ -28,9 +56,8 @@ struct DecodeArgs {
   int block_size, max_blocks_per_seq;
   int64_t num_blocks;
   int dtype;
-  float* ws_ml;  // [B, Hq, P, 2] (max in log2 units, sum)
-  float* ws_o;   // [B, Hq, P, D] unnormalised partial outputs
-  int num_parts; // P
+  float* ws_ml;   // [B, Hq, P, 2] (max in log2 units, sum), P = parts at 512 tokens
+  float* ws_o;    // [B, Hq, P, D] unnormalised partial outputs
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

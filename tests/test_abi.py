@@ -99,15 +99,27 @@ def test_decode_validation(L):
 
 
 def test_decode_workspace_size(L):
-    part = L.pkv_decode_partition_tokens()
-    assert part == 512
-    # one partition -> no workspace
-    assert L.paged_attention_decode_workspace_size(8, 32, 128, part // 16, 16) == 0
+    # one 512-token partition -> no workspace
+    assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == 0
     # 131072-token contexts with bs 128: 256 partitions of (max, sum) + D floats
     got = L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128)
     assert got == 4 * 64 * 256 * (2 + 128) * 4
     assert L.paged_attention_decode_workspace_size(0, 64, 128, 1024, 128) == 0
     assert L.paged_attention_decode_workspace_size(4, 64, 96, 1024, 128) == 0
+
+
+def test_decode_partition_plan(L):
+    f = L.pkv_decode_partition_tokens
+    # long contexts: 512-token partitions
+    assert f(4, 64, 8, 1024, 128, 2) == 512
+    # a batch with one (sequence, head group) row per compute unit and 2048-token
+    # contexts takes whole contexts per workgroup
+    assert f(8, 32, 32, 128, 16, 1) == 2048
+    # too few rows to fill the chip: split
+    assert f(2, 32, 32, 128, 16, 1) == 512
+    # fp32 path always splits at 512
+    assert f(8, 32, 32, 128, 16, 0) == 512
+    assert f(8, 6, 4, 128, 16, 1) == 0           # invalid head counts
 
 
 def varlen(L, **kw):
