@@ -170,6 +170,15 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also waits
+// for every outstanding global load (its fence covers global memory), which
+// would stall on loads prefetched for the next tile.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Merge weight for a partial with running max m against the merged max
 // `mref`, where mref == -inf means "nothing seen yet" (weight 0 for m=-inf).
 __device__ __forceinline__ float safe_max_ref(float m) { return m == -INFINITY ? 0.f : m; }

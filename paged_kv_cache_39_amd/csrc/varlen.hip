@@ -30,25 +30,38 @@ constexpr int kVlRows = 128;      // rows per workgroup = query positions x head
 constexpr int kVlRowsWave = 32;   // two 16-row MFMA tiles per wave
 constexpr int kVlBN = 64;         // keys per KV tile
 
+// K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
+// 16-byte slots: slot s of row r holds chunk s ^ f(r), f a one-bit rotation
+// of r mod (slots per row). With it the K operand reads (16 rows, one chunk
+// each) and the V transpose reads (4 rows x 2 adjacent chunks per 16 lanes)
+// both touch every bank once.
 template <int D>
 struct VlLds {
-  static constexpr int kRowB = D * 2 + 16;        // K tile row pitch (bytes), padded
-  static constexpr int vRowB = kVlBN * 2 + 16;     // V^T tile row pitch (bytes), padded
-  static constexpr int kBytes = kVlBN * kRowB;
-  static constexpr int vBytes = D * vRowB;
+  static constexpr int rowB = D * 2;
+  static constexpr int spr = D / 8;                  // 16-byte slots per row
+  static constexpr int sbits = spr == 16 ? 4 : 3;
+  static constexpr int tileB = kVlBN * rowB;         // one K or V tile
+  static constexpr int stageB = 2 * tileB;           // K and V
+  static __device__ __forceinline__ int f(int r) {
+    const int x = r & (spr - 1);
+    return ((x << 1) | (x >> (sbits - 1))) & (spr - 1);
+  }
+  static __device__ __forceinline__ int slot(int r, int chunk) { return chunk ^ f(r); }
 };
 
 // Locate query tile `t` (0-based over the whole batch, tiles of `bq` rows per
-// sequence) by a wave-wide prefix scan of per-sequence tile counts.
+// sequence) by a wave-wide prefix scan of per-sequence tile counts. Within a
+// sequence the tiles are handed out last first: under the causal mask the
+// last tile sees the most keys, so the heaviest work starts earliest.
 // Returns false when t is past the last tile.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int num_seqs, int bq,
-                                          int t, int lane, int& seq, int& q0) {
+                                          int total_q, int t, int lane, int& seq, int& q0) {
   int base_tiles = 0;
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
     const int s = s0 + lane;
     int nt = 0;
     if (s < num_seqs) {
-      const int lq = cu[s + 1] - cu[s];
+      const int lq = min(cu[s + 1], total_q) - max(0, min(cu[s], total_q));
       nt = lq > 0 ? (lq + bq - 1) / bq : 0;
     }
     int incl = nt;
@@ -62,8 +75,9 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
       const unsigned long long hit = __ballot(base_tiles + incl > t);
       const int first = __builtin_ctzll(hit);
       const int excl = __shfl(incl - nt, first, kWave);
+      const int ntile = __shfl(nt, first, kWave);
       seq = s0 + first;
-      q0 = (t - base_tiles - excl) * bq;
+      q0 = (ntile - 1 - (t - base_tiles - excl)) * bq;
       return true;
     }
     base_tiles += total;
@@ -72,18 +86,21 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
 }
 
 template <class Ty, int D>
-__global__ __launch_bounds__(kVlThreads) void varlen_prefill_kernel(
+__global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu_seqlens_q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2) {
   using L = VlLds<D>;
-  constexpr int KS = D / 32;   // k-steps of the QK product
-  constexpr int ND = D / 16;   // 16-wide dim tiles of the output
-  constexpr int CPT = D / 8;   // 16-byte chunks per K/V row
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[L::kBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[L::vBytes];
+  constexpr int KS = D / 32;                 // k-steps of the QK product
+  constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
+  constexpr int RPI = kWave / L::spr;        // rows per direct-to-LDS load of one wave
+  constexpr int LPT = kVlBN / (kVlWaves * RPI);  // such loads per thread per matrix
+  // lazy rescale: the running max used for the exponentials only moves when
+  // a row max exceeds it by more than 2^8 (P then stays <= 256)
+  constexpr float kRescale = 8.f;
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * L::stageB];
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -95,7 +112,7 @@ __global__ __launch_bounds__(kVlThreads) void varlen_prefill_kernel(
 
   if (wave == 0) {
     int seq = -1, q0 = 0;
-    if (!find_tile(cu_seqlens_q, num_seqs, bq, blockIdx.x, lane, seq, q0)) seq = -1;
+    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, blockIdx.x, lane, seq, q0)) seq = -1;
     if (lane == 0) {
       s_tile[0] = seq;
       s_tile[1] = q0;
@@ -120,161 +137,173 @@ __global__ __launch_bounds__(kVlThreads) void varlen_prefill_kernel(
     q_pos[mt] = q0 + i;
     head[mt] = kvh * group + r % group;
     row_ok[mt] = (i < bq) && (q_pos[mt] < lq);
-    // last key index this row may see (-1: none)
     lim[mt] = row_ok[mt] ? (causal ? min(lk - 1, q_pos[mt] + delta) : lk - 1) : -1;
   }
+
+  // keys this tile needs (up to the largest lim over its rows); keys below
+  // `nomask_end` are visible to every row of the tile
+  const int last_q = min(q0 + bq, lq) - 1;
+  const int kv_end = causal ? min(lk, last_q + delta + 1) : lk;
+  const int nomask_end = causal ? min(lk, q0 + delta + 1) : lk;
+
+  const int row_stride = num_kv_heads * D;
+  const int32_t* bt_row = block_table + (size_t)b * max_blocks_per_seq;
+
+  // Stage keys kv0 .. kv0+63 into stage `st`: the block ids (at most four)
+  // come from wave-uniform scalar loads; each lane fetches one 16-byte chunk
+  // straight into LDS. Keys past Lk fetch the last valid key instead (finite
+  // values whose probabilities are masked to zero).
+  auto stage = [&](int st, int kv0) {
+    const int i0 = kv0 >> log2_bs;
+    int ids[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bi = min(i0 + e, max_blocks_per_seq - 1);
+      ids[e] = __builtin_amdgcn_readfirstlane(bt_row[bi]);
+    }
+    uint8_t* sk = s_kv + st * L::stageB;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int rbase = (j * kVlWaves + wave) * RPI;       // first row of this load
+      const int r = rbase + lane / L::spr;
+      const int key = min(kv0 + r, lk - 1);
+      const int e = (key >> log2_bs) - i0;
+      int blk = e == 0 ? ids[0] : e == 1 ? ids[1] : e == 2 ? ids[2] : ids[3];
+      blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
+      const int chunk = L::slot(r, lane % L::spr);
+      const size_t off =
+          ((size_t)blk * bs + (key & (bs - 1))) * row_stride + kvh * D + chunk * 8;
+      typedef __attribute__((address_space(3))) void lds_void;
+      __builtin_amdgcn_global_load_lds(k_cache + off, (lds_void*)(sk + rbase * L::rowB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v_cache + off,
+                                       (lds_void*)(sk + L::tileB + rbase * L::rowB), 16, 0, 0);
+    }
+  };
+
+  if (kv_end > 0) stage(0, 0);
 
   // Q^T operands (B of S^T = K Q^T): lane holds Q[row][32s + 8*g4 .. +8]
   u32x4_t qb[2][KS];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const bool ok = row_ok[mt];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (ok) {
-        const uint16_t* src = q + ((size_t)(row0 + q_pos[mt]) * num_q_heads + head[mt]) * D +
-                              32 * s + 8 * g4;
-        qb[mt][s] = *reinterpret_cast<const u32x4_t*>(src);
-      } else {
-        qb[mt][s] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      qb[mt][s] = row_ok[mt]
+                      ? load16<false>(q + ((size_t)(row0 + q_pos[mt]) * num_q_heads + head[mt]) * D +
+                                      32 * s + 8 * g4)
+                      : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-
-  // keys this tile needs: up to the largest lim over the tile's rows
-  const int last_q = min(q0 + bq, lq) - 1;
-  const int kv_end = causal ? min(lk, last_q + delta + 1) : lk;
 
   f32x4_t acc[2][ND];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) acc[mt][nd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_use[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
   float l_run[2] = {0.f, 0.f};
 
-  const int row_stride = num_kv_heads * D;
-  const int32_t* bt_row = block_table + (size_t)b * max_blocks_per_seq;
+  // per-lane LDS offsets (within a stage)
+  // K operand, key block n, k-step s: row 16n + l16, chunk 4s + g4
+  // V^T operand: lane i of a 16-lane group -> row 4*g4 + i/4 (+16), chunk
+  // 2nd + (i%4)/2, byte 8*(i%2) within the chunk
+  const int vrow = 4 * g4 + (l16 >> 2);
+  const int vbyte = 8 * (l16 & 1);
+  const int vchunk = (l16 & 3) >> 1;
 
-  for (int kv0 = 0; kv0 < kv_end; kv0 += kVlBN) {
-    // ---- stage K (row-major) and V^T (dim-major) for keys kv0 .. kv0+63 ----
-    __syncthreads();  // previous tile's LDS reads are done
+  int it = 0;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += kVlBN, ++it) {
+    const int cur = it & 1;
+    const bool more = kv0 + kVlBN < kv_end;
+    if (more) stage(cur ^ 1, kv0 + kVlBN);
+    // this tile's loads (issued one iteration earlier) have landed
+    if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPT));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+    const uint8_t* sk = s_kv + cur * L::stageB;
+    const uint8_t* sv = sk + L::tileB;
+    const bool need_mask = kv0 + kVlBN > nomask_end;
+
 #pragma unroll
-    for (int j = 0; j < (kVlBN * CPT) / kVlThreads; ++j) {
-      const int id = j * kVlThreads + tid;
-      const int t = id / CPT, ch = id % CPT;
-      const int key = kv0 + t;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (key < lk) {
-        int blk = bt_row[key >> log2_bs];
-        if (blk >= 0 && blk < num_blocks) {
-          const uint16_t* src = k_cache + ((size_t)blk * bs + (key & (bs - 1))) * row_stride +
-                                kvh * D + ch * 8;
-          v = *reinterpret_cast<const u32x4_t*>(src);
+    for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
+      // ---- S^T = K Q^T for keys kv0 + 32hh .. +32 ----
+      f32x4_t st[2][2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int r = 32 * hh + 16 * n + l16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              sk + r * L::rowB + L::slot(r, 4 * s + g4) * 16);
+          st[n][0] = Mma<Ty>::mfma(a, qb[0][s], st[n][0]);
+          st[n][1] = Mma<Ty>::mfma(a, qb[1][s], st[n][1]);
         }
       }
-      *reinterpret_cast<u32x4_t*>(s_k + t * L::kRowB + ch * 16) = v;
-    }
+      // ---- online softmax; lane's keys: kv0 + 32hh + 16n + 4*g4 + i ----
+      float sv_[2][2][4];
+      float mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-    for (int j = 0; j < (kVlBN / 2 * CPT) / kVlThreads; ++j) {
-      const int id = j * kVlThreads + tid;
-      const int tp = id / CPT, ch = id % CPT;
-      u32x4_t v2[2];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = kv0 + 2 * tp + h;
-        v2[h] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key < lk) {
-          int blk = bt_row[key >> log2_bs];
-          if (blk >= 0 && blk < num_blocks) {
-            const uint16_t* src = v_cache + ((size_t)blk * bs + (key & (bs - 1))) * row_stride +
-                                  kvh * D + ch * 8;
-            v2[h] = *reinterpret_cast<const u32x4_t*>(src);
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = st[n][mt][i] * scale_log2;
+            const int key = kv0 + 32 * hh + 16 * n + 4 * g4 + i;
+            sv_[mt][n][i] = (!need_mask || key <= lim[mt]) ? x : -INFINITY;
+            mx[mt] = fmaxf(mx[mt], sv_[mt][n][i]);
           }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        mx[mt] = fmaxf(mx[mt], shfl_xor_f(mx[mt], 16));
+        mx[mt] = fmaxf(mx[mt], shfl_xor_f(mx[mt], 32));
+      }
+      const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const float mnew = fmaxf(m_use[mt], mx[mt]);
+          const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
+          m_use[mt] = mnew;
+          l_run[mt] *= alpha;
+#pragma unroll
+          for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
         }
       }
-      // element e of the chunk is dim ch*8+e; write (key 2tp, key 2tp+1) as one dword
+      u32x4_t pb[2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = v2[0][w], c = v2[1][w];
-        const uint32_t lo = (a & 0xffffu) | (c << 16);          // dim ch*8 + 2w
-        const uint32_t hi = (a >> 16) | (c & 0xffff0000u);      // dim ch*8 + 2w + 1
-        *reinterpret_cast<uint32_t*>(s_v + (ch * 8 + 2 * w) * L::vRowB + tp * 4) = lo;
-        *reinterpret_cast<uint32_t*>(s_v + (ch * 8 + 2 * w + 1) * L::vRowB + tp * 4) = hi;
+      for (int mt = 0; mt < 2; ++mt) {
+        const float mref = safe_max_ref(m_use[mt]);
+        float pv[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[n][i] = fast_exp2(sv_[mt][n][i] - mref);
+            psum += pv[n][i];
+          }
+        l_run[mt] += psum;
+        pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
+        pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
+        pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
+        pb[mt][3] = Mma<Ty>::pack(pv[1][2], pv[1][3]);
       }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T: 4 key tiles x 2 row tiles ----
-    f32x4_t st[4][2];
+      // ---- O^T += V^T P^T over these 32 keys ----
+      const int r0 = 32 * hh + vrow, r1 = r0 + 16;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      st[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(s_k + (16 * n + l16) * L::kRowB + 64 * s + 16 * g4);
-        st[n][0] = Mma<Ty>::mfma(a, qb[0][s], st[n][0]);
-        st[n][1] = Mma<Ty>::mfma(a, qb[1][s], st[n][1]);
-      }
-    }
-
-    // ---- online softmax per row; lane's keys: kv0 + 16n + 4*g4 + i ----
-    u32x4_t pb[2][2];   // P^T operands for the two 32-key halves
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float sv[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + 16 * n + 4 * g4 + i;
-          const float x = st[n][mt][i] * scale_log2;
-          sv[n][i] = key <= lim[mt] ? x : -INFINITY;
-          mx = fmaxf(mx, sv[n][i]);
-        }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float mnew = fmaxf(m_run[mt], mx);
-      const float mref = safe_max_ref(mnew);
-      const float alpha = fast_exp2(m_run[mt] - mref);
-      m_run[mt] = mnew;
-      float psum = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[n][i] = fast_exp2(sv[n][i] - mref);
-          psum += pv[n][i];
-        }
-      l_run[mt] = l_run[mt] * alpha + psum;
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        pb[mt][kk][0] = Mma<Ty>::pack(pv[2 * kk][0], pv[2 * kk][1]);
-        pb[mt][kk][1] = Mma<Ty>::pack(pv[2 * kk][2], pv[2 * kk][3]);
-        pb[mt][kk][2] = Mma<Ty>::pack(pv[2 * kk + 1][0], pv[2 * kk + 1][1]);
-        pb[mt][kk][3] = Mma<Ty>::pack(pv[2 * kk + 1][2], pv[2 * kk + 1][3]);
-      }
-    }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint8_t* vrow = s_v + (16 * nd + l16) * L::vRowB + (32 * kk + 4 * g4) * 2;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 32);
+      for (int nd = 0; nd < ND; ++nd) {
+        const int c = 2 * nd + vchunk;
+        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot(r0, c) * 16 + vbyte);
+        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot(r1, c) * 16 + vbyte);
         const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[0][nd] = Mma<Ty>::mfma(a, pb[0][kk], acc[0][nd]);
-        acc[1][nd] = Mma<Ty>::mfma(a, pb[1][kk], acc[1][nd]);
+        acc[0][nd] = Mma<Ty>::mfma(a, pb[0], acc[0][nd]);
+        acc[1][nd] = Mma<Ty>::mfma(a, pb[1], acc[1][nd]);
       }
     }
+    lds_barrier();   // every wave is done with this stage before it is refilled
   }
 
   // ---- normalise and store: lane holds O^T[16nd + 4*g4 + i][row] ----
