@@ -29,6 +29,7 @@ constexpr int kVlThreads = kVlWaves * kWave;
 constexpr int kVlRows = 128;      // rows per workgroup = query positions x heads of the group
 constexpr int kVlRowsWave = 32;   // two 16-row MFMA tiles per wave
 constexpr int kVlBN = 64;         // keys per KV tile
+constexpr int kNumXcds = 8;       // accelerator complex dies of an MI355X
 
 // K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
 // 16-byte slots: slot s of row r holds chunk s ^ f(r), f a one-bit rotation
@@ -49,38 +50,73 @@ struct VlLds {
   static __device__ __forceinline__ int slot(int r, int chunk) { return chunk ^ f(r); }
 };
 
-// Locate query tile `t` (0-based over the whole batch, tiles of `bq` rows per
-// sequence) by a wave-wide prefix scan of per-sequence tile counts. Within a
-// sequence the tiles are handed out last first: under the causal mask the
-// last tile sees the most keys, so the heaviest work starts earliest.
-// Returns false when t is past the last tile.
+// Query-tile count of sequence s (0 past the end).
+__device__ __forceinline__ int seq_tiles(const int32_t* __restrict__ cu, int num_seqs, int bq,
+                                         int total_q, int s) {
+  if (s >= num_seqs) return 0;
+  const int lq = min(cu[s + 1], total_q) - max(0, min(cu[s], total_q));
+  return lq > 0 ? (lq + bq - 1) / bq : 0;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// sum_b min(nt_b, cap) over the batch (cap < 0: no cap). `nt0` holds the
+// count of sequence `lane` (the first 64 sequences, read once); further
+// sequences are read from memory.
+__device__ __forceinline__ int tiles_below(const int32_t* __restrict__ cu, int num_seqs, int bq,
+                                           int total_q, int cap, int lane, int nt0) {
+  int sum = cap < 0 ? nt0 : min(nt0, cap);
+  for (int s0 = kWave; s0 < num_seqs; s0 += kWave) {
+    const int nt = seq_tiles(cu, num_seqs, bq, total_q, s0 + lane);
+    sum += cap < 0 ? nt : min(nt, cap);
+  }
+  return wave_sum(sum);
+}
+
+// Locate query tile `t` of one kv head (tiles of `bq` query positions).
+// Tiles are handed out by rank from the end of their sequence: first the
+// last tile of every sequence, then every second-to-last tile, and so on.
+// Under the causal mask a sequence's later tiles see more keys, so the
+// heaviest work is dispatched first and the short tiles fill the tail.
+// One wave runs this; returns false when t is past the last tile.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int num_seqs, int bq,
                                           int total_q, int t, int lane, int& seq, int& q0) {
-  int base_tiles = 0;
+  const int nt0 = seq_tiles(cu, num_seqs, bq, total_q, lane);
+  if (t >= tiles_below(cu, num_seqs, bq, total_q, -1, lane, nt0)) return false;
+  // largest rank j with sum_b min(nt_b, j) <= t
+  int lo = 0, hi = 1;
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
-    const int s = s0 + lane;
-    int nt = 0;
-    if (s < num_seqs) {
-      const int lq = min(cu[s + 1], total_q) - max(0, min(cu[s], total_q));
-      nt = lq > 0 ? (lq + bq - 1) / bq : 0;
-    }
-    int incl = nt;
+    const int nt = s0 == 0 ? nt0 : seq_tiles(cu, num_seqs, bq, total_q, s0 + lane);
+    int m = nt;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (t < base_tiles + total) {
-      const unsigned long long hit = __ballot(base_tiles + incl > t);
-      const int first = __builtin_ctzll(hit);
-      const int excl = __shfl(incl - nt, first, kWave);
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, kWave));
+    hi = max(hi, m + 1);
+  }
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tiles_below(cu, num_seqs, bq, total_q, mid, lane, nt0) <= t) lo = mid;
+    else hi = mid;
+  }
+  const int j = lo;
+  int r = t - tiles_below(cu, num_seqs, bq, total_q, j, lane, nt0);  // r-th sequence with nt > j
+  for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
+    const int nt = s0 == 0 ? nt0 : seq_tiles(cu, num_seqs, bq, total_q, s0 + lane);
+    const unsigned long long has = __ballot(nt > j);
+    const int cnt = __popcll(has);
+    if (r < cnt) {
+      unsigned long long m = has;   // position of the r-th set bit
+      for (int k = 0; k < r; ++k) m &= m - 1;
+      const int first = __builtin_ctzll(m);
       const int ntile = __shfl(nt, first, kWave);
       seq = s0 + first;
-      q0 = (ntile - 1 - (t - base_tiles - excl)) * bq;
+      q0 = (ntile - 1 - j) * bq;
       return true;
     }
-    base_tiles += total;
+    r -= cnt;
   }
   return false;
 }
@@ -91,7 +127,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const int32_t* __restrict__ cu_seqlens_q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
-    int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2) {
+    int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2,
+    int tiles_per_head) {
   using L = VlLds<D>;
   constexpr int KS = D / 32;                 // k-steps of the QK product
   constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
@@ -105,14 +142,23 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int kvh = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2). Renumber them so that every XCD takes a contiguous range of
+  // (kv head, query tile): the tiles that stream one kv head's K/V then
+  // share an L2.
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % kNumXcds, k_in = blockIdx.x / kNumXcds;
+  const int per = nwg / kNumXcds, rem = nwg % kNumXcds;
+  const int logical = xcd * per + min(xcd, rem) + k_in;
+  const int kvh = logical / tiles_per_head;
+  const int tile = logical - kvh * tiles_per_head;
   const int group = num_q_heads / num_kv_heads;
   const int bq = kVlRows / group;   // query positions per tile
   const int bs = 1 << log2_bs;
 
   if (wave == 0) {
     int seq = -1, q0 = 0;
-    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, blockIdx.x, lane, seq, q0)) seq = -1;
+    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, seq, q0)) seq = -1;
     if (lane == 0) {
       s_tile[0] = seq;
       s_tile[1] = q0;
@@ -201,7 +247,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) acc[mt][nd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_use[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
-  float l_run[2] = {0.f, 0.f};
+  // row sums of P, accumulated as O^T of an all-ones V^T: every register of
+  // the lane holds its row's sum
+  f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  const uint32_t one2 = Mma<Ty>::pack(1.f, 1.f);
+  const u32x4_t ones = {one2, one2, one2, one2};
 
   // per-lane LDS offsets (within a stage)
   // K operand, key block n, k-step s: row 16n + l16, chunk 4s + g4
@@ -224,10 +274,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const uint8_t* sv = sk + L::tileB;
     const bool need_mask = kv0 + kVlBN > nomask_end;
 
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
-      // ---- S^T = K Q^T for keys kv0 + 32hh .. +32 ----
-      f32x4_t st[2][2];
+    // S^T = K Q^T for the 32 keys of half hh (two 16-key blocks x two row tiles)
+    auto qk = [&](int hh, f32x4_t (&st)[2][2]) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -241,33 +289,50 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
           st[n][1] = Mma<Ty>::mfma(a, qb[1][s], st[n][1]);
         }
       }
+    };
+    f32x4_t st_cur[2][2], st_next[2][2];
+    qk(0, st_cur);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
+      // the next half's q.k runs on the matrix cores while this half's
+      // softmax runs on the vector ALUs
+      if (hh == 0) qk(1, st_next);
       // ---- online softmax; lane's keys: kv0 + 32hh + 16n + 4*g4 + i ----
-      float sv_[2][2][4];
-      float mx[2] = {-INFINITY, -INFINITY};
+      // Scores stay unscaled: the max is taken on raw q.k (the scale is
+      // positive) and the exponent is one fma, s*scale - m.
+      if (need_mask) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+          for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = st[n][mt][i] * scale_log2;
-            const int key = kv0 + 32 * hh + 16 * n + 4 * g4 + i;
-            sv_[mt][n][i] = (!need_mask || key <= lim[mt]) ? x : -INFINITY;
-            mx[mt] = fmaxf(mx[mt], sv_[mt][n][i]);
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int key = kv0 + 32 * hh + 16 * n + 4 * g4 + i;
+              st_cur[n][mt][i] = key <= lim[mt] ? st_cur[n][mt][i] : -INFINITY;
+            }
+      }
+      // lane-local maxima (raw scores); the row max over the 4 lane groups is
+      // only needed when the running max has to move
+      float mx[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        mx[mt] = fmaxf(mx[mt], shfl_xor_f(mx[mt], 16));
-        mx[mt] = fmaxf(mx[mt], shfl_xor_f(mx[mt], 32));
+        const float a0 = fmaxf(fmaxf(st_cur[0][mt][0], st_cur[0][mt][1]),
+                               fmaxf(st_cur[0][mt][2], st_cur[0][mt][3]));
+        const float a1 = fmaxf(fmaxf(st_cur[1][mt][0], st_cur[1][mt][1]),
+                               fmaxf(st_cur[1][mt][2], st_cur[1][mt][3]));
+        mx[mt] = fmaxf(a0, a1) * scale_log2;
       }
       const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const float mnew = fmaxf(m_use[mt], mx[mt]);
+          float m = mx[mt];
+          m = fmaxf(m, shfl_xor_f(m, 16));
+          m = fmaxf(m, shfl_xor_f(m, 32));
+          const float mnew = fmaxf(m_use[mt], m);
           const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
           m_use[mt] = mnew;
-          l_run[mt] *= alpha;
+          lacc[mt] *= alpha;
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
         }
@@ -275,21 +340,18 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       u32x4_t pb[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const float mref = safe_max_ref(m_use[mt]);
+        const float nref = -safe_max_ref(m_use[mt]);
         float pv[2][4];
-        float psum = 0.f;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[n][i] = fast_exp2(sv_[mt][n][i] - mref);
-            psum += pv[n][i];
-          }
-        l_run[mt] += psum;
+          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], scale_log2, nref));
         pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
         pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
         pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
         pb[mt][3] = Mma<Ty>::pack(pv[1][2], pv[1][3]);
+        // row sums of the rounded P on the matrix cores: a V^T tile of ones
+        lacc[mt] = Mma<Ty>::mfma(ones, pb[mt], lacc[mt]);
       }
       // ---- O^T += V^T P^T over these 32 keys ----
       const int r0 = 32 * hh + vrow, r1 = r0 + 16;
@@ -302,6 +364,13 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         acc[0][nd] = Mma<Ty>::mfma(a, pb[0], acc[0][nd]);
         acc[1][nd] = Mma<Ty>::mfma(a, pb[1], acc[1][nd]);
       }
+      if (hh == 0) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          st_cur[n][0] = st_next[n][0];
+          st_cur[n][1] = st_next[n][1];
+        }
+      }
     }
     lds_barrier();   // every wave is done with this stage before it is refilled
   }
@@ -309,9 +378,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // ---- normalise and store: lane holds O^T[16nd + 4*g4 + i][row] ----
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    float lt = l_run[mt];
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = lacc[mt][0];
     if (!row_ok[mt]) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* dst = out + ((size_t)(row0 + q_pos[mt]) * num_q_heads + head[mt]) * D + 4 * g4;
@@ -331,14 +398,14 @@ static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
   const int bq = kVlRows / group;
   const int64_t tiles = (a.total_q + bq - 1) / bq + a.num_seqs;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)a.head_dim);
-  dim3 grid((unsigned)tiles, a.num_kv_heads);
+  dim3 grid((unsigned)(tiles * a.num_kv_heads));
   hipLaunchKernelGGL((varlen_prefill_kernel<Ty, D>), grid, dim3(kVlThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
                      static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens,
                      a.causal, a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
                      __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks,
-                     scale_log2);
+                     scale_log2, (int)tiles);
   return hipGetLastError();
 }
 
