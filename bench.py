@@ -31,6 +31,8 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_fp16_traffic.json")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak, TFLOP/s
 FLUSH_BYTES = 1 << 30          # read between timed steps (4x the Infinity Cache)
 
@@ -44,6 +46,32 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="only the decode step workload")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     return ap.parse_args()
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter
+    passes (FETCH_SIZE / WRITE_SIZE, scaled by the factors measured on a
+    plain 1 GiB read and a plain 1 GiB fill). None when the kernel sources
+    have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if source_digest(rec["sources"]) != rec["sources_sha256"]:
+        return None, rec
+    kib = rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] + \
+        rec["write_kib_per_dispatch"] * rec["write_scale"]
+    return int(round(kib * 1024)), rec
 
 
 class Timer:
@@ -177,12 +205,18 @@ def main():
         "step_bytes": step_bytes,
         "timed_wall_s": round(wall, 4),
     }
+    traffic, trec = measured_traffic()
     result["roofline"] = {
-        "kernel": "paged_attention_decode (partition pass + reduce), LLaMA-7B-shaped batch",
+        "kernel": "decode_mfma_kernel (one launch per paged_attention_decode call on this batch: "
+                  "8-wave workgroups, one whole 2048-token context each, no split)",
         "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
         "algorithmic_bytes_per_launch": meta.decode_bytes(),
+        "timing": "HIP events around each call on the launch stream (includes ~3-4 us of "
+                  "event/launch overhead; the kernel trace gives the kernel alone)",
     }
+    if trec is not None:
+        result["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)
     del t, new_key, new_val
     torch.cuda.empty_cache()
 

@@ -225,7 +225,7 @@ struct MfLds {
   static constexpr int bytes = totalB > mergeB ? totalB : mergeB;
 };
 
-template <class Ty, int D, int WAVES, int TT>
+template <class Ty, int D, int WAVES, int TT, int PD>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -295,8 +295,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   uint8_t* s_k = s_mem + wave * L::waveB;
   uint8_t* s_v = s_k + L::tileB;
 
-  u32x4_t kr[LPI], vr[LPI];
-  auto fetch = [&](int it) {
+  // register ring of PD tiles: tile it+PD is fetched while tile it is used
+  u32x4_t kr[PD][LPI], vr[PD][LPI];
+  auto fetch = [&](int it, u32x4_t (&kk)[LPI], u32x4_t (&vv)[LPI]) {
 #pragma unroll
     for (int j = 0; j < LPI; ++j) {
       const int t0 = wtok0 + it * TT + j * RPI;           // first row of this load (uniform)
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       const int tok = min(tg + lrow, ntok - 1);
       const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
       const size_t off = ((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off;
-      kr[j] = load16<true>(k_cache + off);
-      vr[j] = load16<true>(v_cache + off);
+      kk[j] = load16<true>(k_cache + off);
+      vv[j] = load16<true>(v_cache + off);
     }
   };
 
@@ -317,15 +318,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   // dims 16nd + 4*(i%4) .. +4, and receives dim 16nd + i of tokens 4*g4 .. +4
   const uint8_t* vt = s_v + (4 * g4 + (l16 >> 2)) * L::rowB + (l16 & 3) * 8;
 
-  if (niter > 0) fetch(0);
-  for (int it = 0; it < niter; ++it) {
-#pragma unroll
-    for (int j = 0; j < LPI; ++j) {
-      *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 16) = kr[j];
-      *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 16) = vr[j];
-    }
-    if (it + 1 < niter) fetch(it + 1);
-
+  auto tile = [&](int it) {
     f32x4_t st[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -382,6 +375,25 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
         const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
         acc[nd] *= alpha;
         acc[nd] = Mma<Ty>::mfma(a, pb, acc[nd]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (u < niter) fetch(u, kr[u], vr[u]);
+  for (int it0 = 0; it0 < niter; it0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int it = it0 + u;
+      if (it < niter) {
+#pragma unroll
+        for (int j = 0; j < LPI; ++j) {
+          *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 16) = kr[u][j];
+          *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 16) = vr[u][j];
+        }
+        if (it + PD < niter) fetch(it + PD, kr[u], vr[u]);
+        tile(it);
       }
     }
   }
@@ -526,7 +538,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
 }
 
-template <class Ty, int D, int WAVES, int TT>
+template <class Ty, int D, int WAVES, int TT, int PD>
 static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
                                   int part_tokens) {
   const int log2_bs = __builtin_ctz(a.block_size);
@@ -534,7 +546,7 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT>), grid, dim3(WAVES * kWave), 0, stream,
+  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD>), grid, dim3(WAVES * kWave), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k_cache),
                      static_cast<const uint16_t*>(a.v_cache), a.block_table, a.context_lens,
@@ -553,8 +565,8 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
     if (group % c == 0) { hpw = c; break; }
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
                                       a.block_size);
-  if (plan.waves == 8) return launch_mfma_cfg<Ty, D, 8, 32>(a, stream, hpw, plan.part_tokens);
-  return launch_mfma_cfg<Ty, D, 4, 16>(a, stream, hpw, plan.part_tokens);
+  if (plan.waves == 8) return launch_mfma_cfg<Ty, D, 8, 32, 1>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16, 1>(a, stream, hpw, plan.part_tokens);
 }
 
 template <int D>
