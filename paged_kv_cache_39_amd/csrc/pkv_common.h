@@ -170,6 +170,36 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Asynchronous 16-byte global -> LDS copy per lane: lane l's 16 bytes land
+// at lds_base + 16*l (lds_base wave-uniform). Issued through inline asm so
+// that the compiler does not track it; the caller waits for completion with
+// an explicit s_waitcnt vmcnt before the data is read. (Tracked by the
+// compiler, a pending copy into LDS makes it wait for every outstanding
+// load before any later LDS access.)
+__device__ __forceinline__ void async_copy16_to_lds(const void* g, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// s_waitcnt encodings (gfx9 family): wait until at most n vector-memory
+// operations of this wave are outstanding (lgkm and exp counters untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Barrier without a memory-model fence: this wave's LDS operations complete
+// (lgkmcnt 0), then s_barrier. Outstanding global loads and LDS copies are
+// not waited for; the compiler is kept from moving memory accesses across.
+__device__ __forceinline__ void barrier_lds_ops() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that orders LDS accesses only. __syncthreads() also waits
 // for every outstanding global load (its fence covers global memory), which
 // would stall on loads prefetched for the next tile.

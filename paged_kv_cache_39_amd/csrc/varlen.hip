@@ -219,10 +219,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       const int chunk = L::slot(r, lane % L::spr);
       const size_t off =
           ((size_t)blk * bs + (key & (bs - 1))) * row_stride + kvh * D + chunk * 8;
-      typedef __attribute__((address_space(3))) void lds_void;
-      __builtin_amdgcn_global_load_lds(k_cache + off, (lds_void*)(sk + rbase * L::rowB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(v_cache + off,
-                                       (lds_void*)(sk + L::tileB + rbase * L::rowB), 16, 0, 0);
+      async_copy16_to_lds(k_cache + off, sk + rbase * L::rowB);
+      async_copy16_to_lds(v_cache + off, sk + L::tileB + rbase * L::rowB);
     }
   };
 
@@ -240,6 +238,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
                       : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+
+  // the queries and the first stage are needed before anything else; waiting
+  // for both here keeps the compiler from placing a full wait later, when
+  // the next stage's copies are in flight
+  wait_vmcnt<0>();
 
   f32x4_t acc[2][ND];
 #pragma unroll
@@ -266,37 +269,63 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const int cur = it & 1;
     const bool more = kv0 + kVlBN < kv_end;
     if (more) stage(cur ^ 1, kv0 + kVlBN);
-    // this tile's loads (issued one iteration earlier) have landed
-    if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPT));
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    lds_barrier();
+    // this tile's copies (issued one iteration earlier) have landed in LDS;
+    // the next tile's stay in flight
+    if (more) wait_vmcnt<2 * LPT>();
+    else wait_vmcnt<0>();
+    barrier_lds_ops();
     const uint8_t* sk = s_kv + cur * L::stageB;
     const uint8_t* sv = sk + L::tileB;
     const bool need_mask = kv0 + kVlBN > nomask_end;
 
-    // S^T = K Q^T for the 32 keys of half hh (two 16-key blocks x two row tiles)
-    auto qk = [&](int hh, f32x4_t (&st)[2][2]) {
+    // Operand reads from LDS are issued a phase ahead of the MFMAs that use
+    // them, so their latency hides behind the softmax arithmetic:
+    //   K operands of half h+1 and V^T operands of half h are read, the
+    //   softmax of half h runs, then q.k of half h+1 and p.v of half h issue.
+    auto read_k = [&](int hh, u32x4_t (&ka)[2][KS]) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int r = 32 * hh + 16 * n + l16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot(r, 4 * s + g4) * 16);
+      }
+    };
+    auto qk = [&](const u32x4_t (&ka)[2][KS], f32x4_t (&st)[2][2]) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         st[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int r = 32 * hh + 16 * n + l16;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              sk + r * L::rowB + L::slot(r, 4 * s + g4) * 16);
-          st[n][0] = Mma<Ty>::mfma(a, qb[0][s], st[n][0]);
-          st[n][1] = Mma<Ty>::mfma(a, qb[1][s], st[n][1]);
+          st[n][0] = Mma<Ty>::mfma(ka[n][s], qb[0][s], st[n][0]);
+          st[n][1] = Mma<Ty>::mfma(ka[n][s], qb[1][s], st[n][1]);
         }
       }
     };
-    f32x4_t st_cur[2][2], st_next[2][2];
-    qk(0, st_cur);
+    auto read_v = [&](int hh, u32x4_t (&va)[ND]) {
+      const int r0 = 32 * hh + vrow, r1 = r0 + 16;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int c = 2 * nd + vchunk;
+        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot(r0, c) * 16 + vbyte);
+        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot(r1, c) * 16 + vbyte);
+        va[nd] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+
+    f32x4_t st_cur[2][2];
+    {
+      u32x4_t ka[2][KS];
+      read_k(0, ka);
+      qk(ka, st_cur);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
-      // the next half's q.k runs on the matrix cores while this half's
-      // softmax runs on the vector ALUs
-      if (hh == 0) qk(1, st_next);
+      u32x4_t ka[2][KS];
+      u32x4_t va[ND];
+      if (hh == 0) read_k(1, ka);
+      read_v(hh, va);
       // ---- online softmax; lane's keys: kv0 + 32hh + 16n + 4*g4 + i ----
       // Scores stay unscaled: the max is taken on raw q.k (the scale is
       // positive) and the exponent is one fma, s*scale - m.
@@ -350,29 +379,21 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
         pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
         pb[mt][3] = Mma<Ty>::pack(pv[1][2], pv[1][3]);
+      }
+      // ---- q.k of the next half, then O^T += V^T P^T over these 32 keys ----
+      if (hh == 0) qk(ka, st_cur);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
         // row sums of the rounded P on the matrix cores: a V^T tile of ones
         lacc[mt] = Mma<Ty>::mfma(ones, pb[mt], lacc[mt]);
       }
-      // ---- O^T += V^T P^T over these 32 keys ----
-      const int r0 = 32 * hh + vrow, r1 = r0 + 16;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const int c = 2 * nd + vchunk;
-        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot(r0, c) * 16 + vbyte);
-        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot(r1, c) * 16 + vbyte);
-        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[0][nd] = Mma<Ty>::mfma(a, pb[0], acc[0][nd]);
-        acc[1][nd] = Mma<Ty>::mfma(a, pb[1], acc[1][nd]);
-      }
-      if (hh == 0) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          st_cur[n][0] = st_next[n][0];
-          st_cur[n][1] = st_next[n][1];
-        }
+        acc[0][nd] = Mma<Ty>::mfma(va[nd], pb[0], acc[0][nd]);
+        acc[1][nd] = Mma<Ty>::mfma(va[nd], pb[1], acc[1][nd]);
       }
     }
-    lds_barrier();   // every wave is done with this stage before it is refilled
+    barrier_lds_ops();   // every wave is done with this stage before it is refilled
   }
 
   // ---- normalise and store: lane holds O^T[16nd + 4*g4 + i][row] ----
