@@ -199,26 +199,48 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // come from wave-uniform scalar loads; each lane fetches one 16-byte chunk
   // straight into LDS. Keys past Lk fetch the last valid key instead (finite
   // values whose probabilities are masked to zero).
+  // per-lane parts of the copy addresses (loop invariant): row r_j of load
+  // j, its swizzled source chunk, and the element offset within a slot row
+  int lrow_[LPT], loff_[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int rbase = (j * kVlWaves + wave) * RPI;
+    lrow_[j] = rbase + lane / L::spr;
+    loff_[j] = kvh * D + L::slot(lrow_[j], lane % L::spr) * 8;
+  }
   auto stage = [&](int st, int kv0) {
+    uint8_t* sk = s_kv + st * L::stageB;
     const int i0 = kv0 >> log2_bs;
+    if (bs >= kVlBN && kv0 + kVlBN <= lk) {
+      // the whole tile lies in one block: a scalar base plus per-lane offsets
+      int blk = __builtin_amdgcn_readfirstlane(bt_row[i0]);
+      blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
+      const size_t base = ((size_t)blk * bs + (kv0 & (bs - 1))) * row_stride;
+      const uint16_t* kb = k_cache + base;
+      const uint16_t* vb = v_cache + base;
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int rbase = (j * kVlWaves + wave) * RPI;
+        const int off = lrow_[j] * row_stride + loff_[j];
+        async_copy16_to_lds(kb + off, sk + rbase * L::rowB);
+        async_copy16_to_lds(vb + off, sk + L::tileB + rbase * L::rowB);
+      }
+      return;
+    }
     int ids[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int bi = min(i0 + e, max_blocks_per_seq - 1);
       ids[e] = __builtin_amdgcn_readfirstlane(bt_row[bi]);
     }
-    uint8_t* sk = s_kv + st * L::stageB;
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      const int rbase = (j * kVlWaves + wave) * RPI;       // first row of this load
-      const int r = rbase + lane / L::spr;
-      const int key = min(kv0 + r, lk - 1);
+      const int rbase = (j * kVlWaves + wave) * RPI;
+      const int key = min(kv0 + lrow_[j], lk - 1);
       const int e = (key >> log2_bs) - i0;
       int blk = e == 0 ? ids[0] : e == 1 ? ids[1] : e == 2 ? ids[2] : ids[3];
       blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
-      const int chunk = L::slot(r, lane % L::spr);
-      const size_t off =
-          ((size_t)blk * bs + (key & (bs - 1))) * row_stride + kvh * D + chunk * 8;
+      const size_t off = ((size_t)blk * bs + (key & (bs - 1))) * row_stride + loff_[j];
       async_copy16_to_lds(k_cache + off, sk + rbase * L::rowB);
       async_copy16_to_lds(v_cache + off, sk + L::tileB + rbase * L::rowB);
     }

@@ -111,3 +111,20 @@ def test_long_context_decode_sampled():
     pairs = [(b, h) for b in range(4) for h in rng.choice(64, size=3, replace=False).tolist()]
     pairs += [(b, 8 * b + 7) for b in range(4)]
     check_decode(case, pairs=sorted(set(pairs)))
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 64)])
+def test_decode_whole_context_plan_edge_lengths(dtype, d):
+    """>= 256 (sequence, head group) rows with contexts <= 2048: one 8-wave
+    workgroup per context, no split. Edge lengths around tiles and blocks."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 1023, 1024, 2047, 2048, 1500]
+    case = wl.decode_case(900 + d, lens, 32, 16, d, 16, dtype, spare=0.2)
+    assert binding.decode_partition_tokens(len(lens), 32, 16, case.max_blocks_per_seq, 16,
+                                           torch.float16) == 2048
+    check_decode(case)
+
+
+def test_decode_group_larger_than_one_tile():
+    """64 query heads per kv head: four 16-head workgroups share a kv head."""
+    case = wl.decode_case(910, [700, 33, 1600], 64, 1, 128, 32, "bf16")
+    check_decode(case)

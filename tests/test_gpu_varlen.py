@@ -76,3 +76,14 @@ def test_packed_prefill_named_workload():
     case = wl.workload(4)
     rows = [(r, h) for r in range(case.q.shape[0]) for h in (0, 5, 13, 31)]
     check_varlen(case, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_varlen_mixed_decode_and_chunked_prefill(dtype):
+    """One packed call mixing decode rows (Lq = 1 over a long cache),
+    multi-token decode (Lq = 4), a chunked prefill continuing a cached
+    prefix, and a fresh prompt: the bottom-right causal reading."""
+    ql = [1, 1, 4, 200, 333, 1]
+    kl = [1500, 7, 900, 900, 333, 64]
+    case = wl.varlen_case(950, ql, kl, 32, 8, 128, 16, dtype, causal=True)
+    check_varlen(case)
