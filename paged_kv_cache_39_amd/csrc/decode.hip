@@ -221,7 +221,9 @@ struct MfLds {
   static constexpr int tileB = TT * rowB;             // one K or V tile
   static constexpr int waveB = 2 * tileB;
   static constexpr int totalB = WAVES * waveB;
-  static constexpr int mergeB = WAVES * 16 * (D + 2) * 4;
+  static constexpr int oRow = D + 4;                  // merge row pitch (floats): rows of
+                                                      // successive heads start 4 banks apart
+  static constexpr int mergeB = WAVES * 16 * (2 + oRow) * 4;
   static constexpr int bytes = totalB > mergeB ? totalB : mergeB;
 };
 
@@ -403,15 +405,17 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   l_run += shfl_xor_f(l_run, 32);
   __syncthreads();  // every wave is done with its K/V tiles
   float* s_ml = reinterpret_cast<float*>(s_mem);                 // [wave][16][2]
-  float* s_o = s_ml + WAVES * 16 * 2;                            // [wave][16][D]
-  if (g4 == 0) {
-    s_ml[(wave * 16 + l16) * 2 + 0] = m_run;
-    s_ml[(wave * 16 + l16) * 2 + 1] = l_run;
+  float* s_o = s_ml + WAVES * 16 * 2;                            // [wave][16][oRow]
+  // only lanes of real heads write; each writes its 4 consecutive dims at once
+  if (head_ok) {
+    if (g4 == 0) {
+      s_ml[(wave * 16 + l16) * 2 + 0] = m_run;
+      s_ml[(wave * 16 + l16) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+      *reinterpret_cast<f32x4_t*>(s_o + (wave * 16 + l16) * L::oRow + 16 * nd + 4 * g4) = acc[nd];
   }
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[(wave * 16 + l16) * D + 16 * nd + 4 * g4 + i] = acc[nd][i];
   __syncthreads();
 
   for (int idx = tid; idx < heads_per_wg * D; idx += NT) {
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     for (int w = 0; w < WAVES; ++w) {
       const float wt = fast_exp2(s_ml[(w * 16 + hh) * 2] - mr);
       ll += s_ml[(w * 16 + hh) * 2 + 1] * wt;
-      a += s_o[(w * 16 + hh) * D + d] * wt;
+      a += s_o[(w * 16 + hh) * L::oRow + d] * wt;
     }
     const size_t bh = (size_t)b * num_q_heads + h0 + hh;
     if (nparts_b == 1) {
