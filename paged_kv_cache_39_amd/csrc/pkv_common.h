@@ -170,14 +170,31 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Asynchronous 16-byte global -> LDS copy per lane: lane l's 16 bytes land
-// at lds_base + 16*l (lds_base wave-uniform). Issued through inline asm so
-// that the compiler does not track it; the caller waits for completion with
-// an explicit s_waitcnt vmcnt before the data is read. (Tracked by the
-// compiler, a pending copy into LDS makes it wait for every outstanding
-// load before any later LDS access.)
-__device__ __forceinline__ void async_copy16_to_lds(const void* g, const void* lds_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+// Asynchronous 16-byte global -> LDS copies per lane: lane l's 16 bytes land
+// at LDS byte address lds + 16*l (lds wave-uniform). Issued through inline
+// asm so that the compiler does not track them; the caller waits for
+// completion with an explicit s_waitcnt vmcnt before the data is read.
+// (Tracked by the compiler, a pending copy into LDS makes it wait for every
+// outstanding load before any later LDS access.)
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Source = wave-uniform base + per-lane unsigned 32-bit byte offset.
+__device__ __forceinline__ void async_copy16_to_lds(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // (the builtin returns int: zero-extend both halves)
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Source = per-lane 64-bit address.
+__device__ __forceinline__ void async_copy16_to_lds(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * L::stageB];
   __shared__ int s_tile[2];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps derived addresses scalar
   const int l16 = lane & 15, g4 = lane >> 4;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2). Renumber them so that every XCD takes a contiguous range of
@@ -195,54 +196,73 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int row_stride = num_kv_heads * D;
   const int32_t* bt_row = block_table + (size_t)b * max_blocks_per_seq;
 
-  // Stage keys kv0 .. kv0+63 into stage `st`: the block ids (at most four)
-  // come from wave-uniform scalar loads; each lane fetches one 16-byte chunk
-  // straight into LDS. Keys past Lk fetch the last valid key instead (finite
-  // values whose probabilities are masked to zero).
-  // per-lane parts of the copy addresses (loop invariant): row r_j of load
-  // j, its swizzled source chunk, and the element offset within a slot row
+  // Stage keys kv0 .. kv0+63 into stage `st`: each lane fetches one 16-byte
+  // chunk straight into LDS. A copy instruction covers RPI consecutive keys,
+  // which always lie in one cache block, so its source is a wave-uniform
+  // block address (from a scalar load of the block id) plus a loop-invariant
+  // 32-bit lane offset. In the last tile, keys past Lk fetch the last valid
+  // key instead (finite values whose probabilities are masked to zero).
+  // per-lane parts (loop invariant): row within the copy, swizzled source
+  // chunk, kv head -> byte offset from the copy's first row
+  const uint32_t row_bytes = (uint32_t)row_stride * 2u;
+  uint32_t voff_[LPT];
   int lrow_[LPT], loff_[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int rbase = (j * kVlWaves + wave) * RPI;
     lrow_[j] = rbase + lane / L::spr;
     loff_[j] = kvh * D + L::slot(lrow_[j], lane % L::spr) * 8;
+    voff_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loff_[j] * 2u;
   }
+  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k_cache);
+  const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(v_cache);
+  const uint32_t lds_kv = lds_address(s_kv);
+  auto block_of = [&](int i) {   // validated block id of table entry i (wave-uniform)
+    const int blk = __builtin_amdgcn_readfirstlane(bt_row[i]);
+    return (blk >= 0 && blk < num_blocks) ? blk : 0;
+  };
   auto stage = [&](int st, int kv0) {
-    uint8_t* sk = s_kv + st * L::stageB;
-    const int i0 = kv0 >> log2_bs;
-    if (bs >= kVlBN && kv0 + kVlBN <= lk) {
-      // the whole tile lies in one block: a scalar base plus per-lane offsets
-      int blk = __builtin_amdgcn_readfirstlane(bt_row[i0]);
-      blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
-      const size_t base = ((size_t)blk * bs + (kv0 & (bs - 1))) * row_stride;
-      const uint16_t* kb = k_cache + base;
-      const uint16_t* vb = v_cache + base;
+    const uint32_t lds_st = lds_kv + (uint32_t)(st * L::stageB);
+    if (kv0 + kVlBN <= lk) {
+      if (bs >= kVlBN) {   // the whole tile lies in one block
+        const size_t base =
+            ((size_t)block_of(kv0 >> log2_bs) * bs + (kv0 & (bs - 1))) * (size_t)row_bytes;
 #pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int rbase = (j * kVlWaves + wave) * RPI;
-        const int off = lrow_[j] * row_stride + loff_[j];
-        async_copy16_to_lds(kb + off, sk + rbase * L::rowB);
-        async_copy16_to_lds(vb + off, sk + L::tileB + rbase * L::rowB);
+        for (int j = 0; j < LPT; ++j) {
+          const int rbase = (j * kVlWaves + wave) * RPI;
+          const size_t src = base + (size_t)rbase * row_bytes;
+          async_copy16_to_lds(kbytes + src, voff_[j], lds_st + rbase * L::rowB);
+          async_copy16_to_lds(vbytes + src, voff_[j], lds_st + L::tileB + rbase * L::rowB);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+          const int rbase = (j * kVlWaves + wave) * RPI;
+          const int key = kv0 + rbase;
+          const size_t src = ((size_t)block_of(key >> log2_bs) * bs + (key & (bs - 1))) *
+                             (size_t)row_bytes;
+          async_copy16_to_lds(kbytes + src, voff_[j], lds_st + rbase * L::rowB);
+          async_copy16_to_lds(vbytes + src, voff_[j], lds_st + L::tileB + rbase * L::rowB);
+        }
       }
       return;
     }
+    // the tile's keys span at most four blocks (block_size >= 16): their ids
+    // come from scalar loads (a per-lane load would make the next vmcnt wait
+    // cover the copies in flight)
+    const int i0 = kv0 >> log2_bs;
     int ids[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int bi = min(i0 + e, max_blocks_per_seq - 1);
-      ids[e] = __builtin_amdgcn_readfirstlane(bt_row[bi]);
-    }
+    for (int e = 0; e < 4; ++e) ids[e] = block_of(min(i0 + e, max_blocks_per_seq - 1));
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int rbase = (j * kVlWaves + wave) * RPI;
       const int key = min(kv0 + lrow_[j], lk - 1);
       const int e = (key >> log2_bs) - i0;
-      int blk = e == 0 ? ids[0] : e == 1 ? ids[1] : e == 2 ? ids[2] : ids[3];
-      blk = (blk >= 0 && blk < num_blocks) ? blk : 0;
+      const int blk = e == 0 ? ids[0] : e == 1 ? ids[1] : e == 2 ? ids[2] : ids[3];
       const size_t off = ((size_t)blk * bs + (key & (bs - 1))) * row_stride + loff_[j];
-      async_copy16_to_lds(k_cache + off, sk + rbase * L::rowB);
-      async_copy16_to_lds(v_cache + off, sk + L::tileB + rbase * L::rowB);
+      async_copy16_to_lds(k_cache + off, lds_st + rbase * L::rowB);
+      async_copy16_to_lds(v_cache + off, lds_st + L::tileB + rbase * L::rowB);
     }
   };
 
@@ -272,6 +292,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) acc[mt][nd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_use[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
+  float nref[2] = {0.f, 0.f};                // -safe_max_ref(m_use): the exponent offset
   // row sums of P, accumulated as O^T of an all-ones V^T: every register of
   // the lane holds its row's sum
   f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -352,26 +373,27 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       // Scores stay unscaled: the max is taken on raw q.k (the scale is
       // positive) and the exponent is one fma, s*scale - m.
       if (need_mask) {
+        // key kv0 + 32hh + 16n + 4*g4 + i is visible iff 32hh + 16n + i <= thr
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+          const int thr = lim[mt] - kv0 - 4 * g4;
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kv0 + 32 * hh + 16 * n + 4 * g4 + i;
-              st_cur[n][mt][i] = key <= lim[mt] ? st_cur[n][mt][i] : -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i)
+              st_cur[n][mt][i] = 32 * hh + 16 * n + i <= thr ? st_cur[n][mt][i] : -INFINITY;
+        }
       }
       // lane-local maxima (raw scores); the row max over the 4 lane groups is
       // only needed when the running max has to move
+      // (maximum, not fmax: no NaN canonicalisation of the MFMA results)
       float mx[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const float a0 = fmaxf(fmaxf(st_cur[0][mt][0], st_cur[0][mt][1]),
-                               fmaxf(st_cur[0][mt][2], st_cur[0][mt][3]));
-        const float a1 = fmaxf(fmaxf(st_cur[1][mt][0], st_cur[1][mt][1]),
-                               fmaxf(st_cur[1][mt][2], st_cur[1][mt][3]));
-        mx[mt] = fmaxf(a0, a1) * scale_log2;
+        float a = st_cur[0][mt][0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) a = __builtin_elementwise_maximum(a, st_cur[k >> 2][mt][k & 3]);
+        mx[mt] = a * scale_log2;
       }
       const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
@@ -383,6 +405,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
           const float mnew = fmaxf(m_use[mt], m);
           const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
           m_use[mt] = mnew;
+          nref[mt] = -safe_max_ref(mnew);
           lacc[mt] *= alpha;
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
@@ -391,12 +414,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       u32x4_t pb[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const float nref = -safe_max_ref(m_use[mt]);
         float pv[2][4];
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], scale_log2, nref));
+          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], scale_log2, nref[mt]));
         pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
         pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
         pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
