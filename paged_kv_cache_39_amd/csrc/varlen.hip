@@ -32,22 +32,27 @@ constexpr int kVlBN = 64;         // keys per KV tile
 constexpr int kNumXcds = 8;       // accelerator complex dies of an MI355X
 
 // K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
-// 16-byte slots: slot s of row r holds chunk s ^ f(r), f a one-bit rotation
-// of r mod (slots per row). With it the K operand reads (16 rows, one chunk
-// each) and the V transpose reads (4 rows x 2 adjacent chunks per 16 lanes)
-// both touch every bank once.
+// 16-byte slots: slot s of row r holds chunk s ^ f(r). The functions were
+// chosen with the LDS bank-conflict counter on gfx950 (a conflict-free
+// 16-byte read of a wave takes 4 LDS cycles, an 8-byte transpose read 2):
+//   K operand reads (ds_read_b128, 16 rows x one chunk): f(r) = r mod spr;
+//   V^T transpose reads (ds_read_b64_tr_b16, 4 rows x 2 adjacent chunks per
+//   16 lanes): f(r) = r mod 8 at D = 64, and at D = 128 a one-bit rotation
+//   of r mod 16 (plain r mod 16 conflicts 2-way there, as the rotation does
+//   for the K reads).
 template <int D>
 struct VlLds {
   static constexpr int rowB = D * 2;
   static constexpr int spr = D / 8;                  // 16-byte slots per row
-  static constexpr int sbits = spr == 16 ? 4 : 3;
   static constexpr int tileB = kVlBN * rowB;         // one K or V tile
   static constexpr int stageB = 2 * tileB;           // K and V
-  static __device__ __forceinline__ int f(int r) {
+  static __device__ __forceinline__ int fk(int r) { return r & (spr - 1); }
+  static __device__ __forceinline__ int fv(int r) {
     const int x = r & (spr - 1);
-    return ((x << 1) | (x >> (sbits - 1))) & (spr - 1);
+    return spr == 16 ? (((x << 1) | (x >> 3)) & 15) : x;
   }
-  static __device__ __forceinline__ int slot(int r, int chunk) { return chunk ^ f(r); }
+  static __device__ __forceinline__ int slot_k(int r, int chunk) { return chunk ^ fk(r); }
+  static __device__ __forceinline__ int slot_v(int r, int chunk) { return chunk ^ fv(r); }
 };
 
 // Query-tile count of sequence s (0 past the end).
@@ -83,9 +88,10 @@ __device__ __forceinline__ int tiles_below(const int32_t* __restrict__ cu, int n
 // Under the causal mask a sequence's later tiles see more keys, so the
 // heaviest work is dispatched first and the short tiles fill the tail.
 // One wave runs this; returns false when t is past the last tile.
+// `nt0` is the tile count of sequence `lane` (0 past the batch).
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int num_seqs, int bq,
-                                          int total_q, int t, int lane, int& seq, int& q0) {
-  const int nt0 = seq_tiles(cu, num_seqs, bq, total_q, lane);
+                                          int total_q, int t, int lane, int nt0, int& seq,
+                                          int& q0) {
   if (t >= tiles_below(cu, num_seqs, bq, total_q, -1, lane, nt0)) return false;
   // largest rank j with sum_b min(nt_b, j) <= t
   int lo = 0, hi = 1;
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // a row max exceeds it by more than 2^8 (P then stays <= 256)
   constexpr float kRescale = 8.f;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * L::stageB];
-  __shared__ int s_tile[2];
+  __shared__ int s_tile[5];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps derived addresses scalar
@@ -157,21 +163,43 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int bq = kVlRows / group;   // query positions per tile
   const int bs = 1 << log2_bs;
 
+  // Wave 0 locates the tile. Lane s first reads sequence s's metadata
+  // (first row, Lq, Lk) in one round trip; the tile's sequence then takes
+  // its metadata from that lane.
   if (wave == 0) {
-    int seq = -1, q0 = 0;
-    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, seq, q0)) seq = -1;
+    int my_r0 = 0, my_lq = 0, my_lk = 0;
+    if (lane < num_seqs) {
+      my_r0 = max(0, min(cu_seqlens_q[lane], total_q));
+      my_lq = max(0, min(cu_seqlens_q[lane + 1], total_q) - my_r0);
+      my_lk = max(0, min(seq_lens[lane], max_blocks_per_seq << log2_bs));
+    }
+    const int nt0 = my_lq > 0 ? (my_lq + bq - 1) / bq : 0;
+    int seq = -1, q0 = 0, r0 = 0, lq_ = 0, lk_ = 0;
+    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)) seq = -1;
+    if (seq >= 0 && seq < kWave) {
+      r0 = __shfl(my_r0, seq, kWave);
+      lq_ = __shfl(my_lq, seq, kWave);
+      lk_ = __shfl(my_lk, seq, kWave);
+    } else if (seq >= kWave) {
+      r0 = max(0, min(cu_seqlens_q[seq], total_q));
+      lq_ = max(0, min(cu_seqlens_q[seq + 1], total_q) - r0);
+      lk_ = max(0, min(seq_lens[seq], max_blocks_per_seq << log2_bs));
+    }
     if (lane == 0) {
       s_tile[0] = seq;
       s_tile[1] = q0;
+      s_tile[2] = r0;
+      s_tile[3] = lq_;
+      s_tile[4] = lk_;
     }
   }
-  __syncthreads();
+  barrier_lds_ops();
   const int b = s_tile[0];
   if (b < 0) return;
   const int q0 = s_tile[1];
-  const int row0 = max(0, min(cu_seqlens_q[b], total_q));
-  const int lq = max(0, min(cu_seqlens_q[b + 1], total_q) - row0);
-  const int lk = max(0, min(seq_lens[b], max_blocks_per_seq << log2_bs));
+  const int row0 = s_tile[2];
+  const int lq = s_tile[3];
+  const int lk = s_tile[4];
   const int delta = lk - lq;
 
   // rows of this lane: r = wave*32 + mt*16 + l16 -> (query i = r / group, head r % group)
@@ -205,14 +233,17 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // per-lane parts (loop invariant): row within the copy, swizzled source
   // chunk, kv head -> byte offset from the copy's first row
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;
-  uint32_t voff_[LPT];
-  int lrow_[LPT], loff_[LPT];
+  uint32_t voffk_[LPT], voffv_[LPT];
+  int lrow_[LPT], loffk_[LPT], loffv_[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int rbase = (j * kVlWaves + wave) * RPI;
     lrow_[j] = rbase + lane / L::spr;
-    loff_[j] = kvh * D + L::slot(lrow_[j], lane % L::spr) * 8;
-    voff_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loff_[j] * 2u;
+    // the lane's LDS slot is lane % spr; it holds chunk slot ^ f(row)
+    loffk_[j] = kvh * D + L::slot_k(lrow_[j], lane % L::spr) * 8;
+    loffv_[j] = kvh * D + L::slot_v(lrow_[j], lane % L::spr) * 8;
+    voffk_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loffk_[j] * 2u;
+    voffv_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loffv_[j] * 2u;
   }
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k_cache);
   const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(v_cache);
@@ -231,8 +262,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         for (int j = 0; j < LPT; ++j) {
           const int rbase = (j * kVlWaves + wave) * RPI;
           const size_t src = base + (size_t)rbase * row_bytes;
-          async_copy16_to_lds(kbytes + src, voff_[j], lds_st + rbase * L::rowB);
-          async_copy16_to_lds(vbytes + src, voff_[j], lds_st + L::tileB + rbase * L::rowB);
+          async_copy16_to_lds(kbytes + src, voffk_[j], lds_st + rbase * L::rowB);
+          async_copy16_to_lds(vbytes + src, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
         }
       } else {
 #pragma unroll
@@ -241,8 +272,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
           const int key = kv0 + rbase;
           const size_t src = ((size_t)block_of(key >> log2_bs) * bs + (key & (bs - 1))) *
                              (size_t)row_bytes;
-          async_copy16_to_lds(kbytes + src, voff_[j], lds_st + rbase * L::rowB);
-          async_copy16_to_lds(vbytes + src, voff_[j], lds_st + L::tileB + rbase * L::rowB);
+          async_copy16_to_lds(kbytes + src, voffk_[j], lds_st + rbase * L::rowB);
+          async_copy16_to_lds(vbytes + src, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
         }
       }
       return;
@@ -260,9 +291,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       const int key = min(kv0 + lrow_[j], lk - 1);
       const int e = (key >> log2_bs) - i0;
       const int blk = e == 0 ? ids[0] : e == 1 ? ids[1] : e == 2 ? ids[2] : ids[3];
-      const size_t off = ((size_t)blk * bs + (key & (bs - 1))) * row_stride + loff_[j];
-      async_copy16_to_lds(k_cache + off, lds_st + rbase * L::rowB);
-      async_copy16_to_lds(v_cache + off, lds_st + L::tileB + rbase * L::rowB);
+      const size_t off = ((size_t)blk * bs + (key & (bs - 1))) * row_stride;
+      async_copy16_to_lds(k_cache + off + loffk_[j], lds_st + rbase * L::rowB);
+      async_copy16_to_lds(v_cache + off + loffv_[j], lds_st + L::tileB + rbase * L::rowB);
     }
   };
 
@@ -331,7 +362,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         const int r = 32 * hh + 16 * n + l16;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot(r, 4 * s + g4) * 16);
+          ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot_k(r, 4 * s + g4) * 16);
       }
     };
     auto qk = [&](const u32x4_t (&ka)[2][KS], f32x4_t (&st)[2][2]) {
@@ -351,8 +382,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
         const int c = 2 * nd + vchunk;
-        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot(r0, c) * 16 + vbyte);
-        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot(r1, c) * 16 + vbyte);
+        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot_v(r0, c) * 16 + vbyte);
+        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot_v(r1, c) * 16 + vbyte);
         va[nd] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
     };
