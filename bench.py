@@ -252,24 +252,33 @@ def main():
                              "bytes": m.decode_bytes()}
             del tt
             torch.cuda.empty_cache()
-        m = wl.workload(4, values=False)
-        dtp = tdt(m.dtype)
-        k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
-        v = torch.randn_like(k)
-        q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp, device=dev)
-        out = torch.empty_like(q)
-        cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
-        ms = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
-                        n_extra)
-        mu = statistics.mean(ms)
-        fl = m.prefill_flops()
-        extra[m.name] = {"us": round(mu * 1e3, 2), "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
-                         "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "flops": fl, "total_q": int(m.cu_seqlens_q[-1])}
-        result["prefill_tflops"] = extra[m.name]["tflops"]
+        for c in (4, 6):
+            # 4: packed causal prefill; 6: decode + multi-token decode + chunked
+            # prefill rows in one packed call (its KV GB/s is reported as well)
+            m = wl.workload(c, values=False)
+            dtp = tdt(m.dtype)
+            k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
+            v = torch.randn_like(k)
+            q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp,
+                            device=dev)
+            out = torch.empty_like(q)
+            cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
+            ms = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
+                            n_extra)
+            mu = statistics.mean(ms)
+            fl = m.prefill_flops()
+            extra[m.name] = {"us": round(mu * 1e3, 2),
+                             "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
+                             "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                             "flops": fl, "total_q": int(m.cu_seqlens_q[-1])}
+            if c == 6:
+                extra[m.name]["kv_gbs"] = round(m.kv_bytes_read() / (mu * 1e-3) / 1e9, 1)
+                extra[m.name]["kv_bytes"] = m.kv_bytes_read()
+            if c == 4:
+                result["prefill_tflops"] = extra[m.name]["tflops"]
+            del k, v, q, out
+            torch.cuda.empty_cache()
         result["other_workloads"] = extra
-        del k, v, q, out
-        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()

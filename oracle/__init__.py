@@ -16,3 +16,9 @@ from .paged_attention import (  # noqa: F401
     widen,
     write_kv,
 )
+from .int8_kv import (  # noqa: F401
+    decode_int8,
+    dequantize_int8,
+    quantize_int8,
+    write_kv_int8,
+)

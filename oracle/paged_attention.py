@@ -63,6 +63,10 @@ def widen(arr: np.ndarray, dtype: str, compute=np.float64) -> np.ndarray:
             raise TypeError("bf16 storage must be uint16 bit patterns")
         f32 = (arr.astype(np.uint32) << np.uint32(16)).view(np.float32)
         return f32.astype(compute)
+    if dtype == "f64":   # already real numbers (e.g. a dequantised int8 pool)
+        if arr.dtype != np.float64:
+            raise TypeError(f"f64 data must be float64, got {arr.dtype}")
+        return arr.astype(compute)
     want = _STORAGE[dtype]
     if arr.dtype != want:
         raise TypeError(f"{dtype} storage must be {want}, got {arr.dtype}")
@@ -150,16 +154,18 @@ def softmax_attention(q_vec, keys, values, scale):
 
 
 def decode(q, k_cache, v_cache, block_table, context_lens, block_size, scale,
-           dtype, compute=np.float64, pairs=None, return_weights=False):
+           dtype, compute=np.float64, pairs=None, return_weights=False, kv_dtype=None):
     """Single-token paged decode.
 
     q: [B, Hq, D]; caches [NB, bs, Hkv, D] in ``dtype`` storage.
     For each sequence b and query head h (kv head h // (Hq // Hkv)), the
     query attends over the ``context_lens[b]`` tokens read through
     ``block_table[b]``. ``pairs`` optionally restricts the work to a list of
-    (b, h); the other rows of the result are left as NaN.
+    (b, h); the other rows of the result are left as NaN. ``kv_dtype``
+    (default ``dtype``) is the storage of the caches when it differs from q's.
     Returns out [B, Hq, D] in ``compute`` (and weights per (b, h) if asked).
     """
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     bsz, hq, d = q.shape
     hkv = k_cache.shape[2]
     if hq % hkv:
@@ -181,8 +187,8 @@ def decode(q, k_cache, v_cache, block_table, context_lens, block_size, scale,
             v_seq = gather_kv(v_cache, block_table[b], n, block_size)
         for kvh in kv_needed:
             if n > 0:
-                keys = widen(np.ascontiguousarray(k_seq[:, kvh, :]), dtype, compute)
-                vals = widen(np.ascontiguousarray(v_seq[:, kvh, :]), dtype, compute)
+                keys = widen(np.ascontiguousarray(k_seq[:, kvh, :]), kv_dtype, compute)
+                vals = widen(np.ascontiguousarray(v_seq[:, kvh, :]), kv_dtype, compute)
             else:
                 keys = np.zeros((0, d), dtype=compute)
                 vals = np.zeros((0, d), dtype=compute)

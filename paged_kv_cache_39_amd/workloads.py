@@ -9,7 +9,7 @@ contains no attention arithmetic.
 Storage conventions: "f32" -> numpy.float32, "f16" -> numpy.float16,
 "bf16" -> numpy.uint16 bit patterns (round-to-nearest-even from float32).
 
-The five named workloads follow the shapes of the pages' LLaMA-7B-class runs
+The named workloads follow the shapes of the pages' LLaMA-7B-class runs
 (32 heads x head_dim 128, batch 8 at 2048 tokens), plus GQA, ragged,
 packed-prefill and long-context variants. Draw order per workload:
 lengths -> block permutation -> q -> K -> V, from numpy.random.default_rng.
@@ -215,7 +215,7 @@ def log_uniform_lengths(rng, n, lo, hi):
 
 
 # ---------------------------------------------------------------------------
-# the five named workloads
+# the named workloads
 # ---------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -224,11 +224,23 @@ WORKLOADS = {
     3: "ragged GQA decode: batch 32, ctx U{50..2000}, 32/8 heads, D 128, bs 32, bf16",
     4: "packed varlen causal prefill: 16 seqs, len log-U[64, 2048], 32/8 heads, D 128, bs 128, bf16",
     5: "long-context split-KV decode: batch 4 x ctx 131072, 64/8 heads, D 128, bs 128, pool 4096, bf16",
+    6: "mixed varlen batch: 24 decode (Lq 1) + 6 multi-token decode (Lq 4), ctx U{512..4096}, "
+       "+ 2 chunked prefills (Lq 512 over Lk 2048); 32/8 heads, D 128, bs 16, bf16",
 }
 
 
+def _mixed_lengths(rng):
+    """Query / KV lengths of the mixed batch: 24 single-token decodes and 6
+    four-token decodes over contexts U{512..4096}, then two 512-token chunks
+    continuing 1536 cached tokens."""
+    ctx = rng.integers(512, 4097, size=30).tolist()
+    ql = [1] * 24 + [4] * 6 + [512, 512]
+    kl = ctx + [2048, 2048]
+    return ql, kl
+
+
 def workload(c: int, values: bool = True) -> PagedCase:
-    """Named workload ``c`` (1..5), seeded with 1000 + c. ``values=False``
+    """Named workload ``c`` (1..6), seeded with 1000 + c. ``values=False``
     returns only the metadata (lengths, block table, slots)."""
     seed = 1000 + c
     if c == 1:
@@ -249,4 +261,14 @@ def workload(c: int, values: bool = True) -> PagedCase:
     if c == 5:
         return decode_case(seed, [131072] * 4, 64, 8, 128, 128, "bf16", num_blocks=4096,
                            name="long_ctx_splitkv_decode_bf16_b4_ctx131072", values=values)
+    if c == 6:
+        box = {}
+
+        def qlens(rng):
+            box["ql"], box["kl"] = _mixed_lengths(rng)
+            return box["ql"]
+
+        return varlen_case(seed, qlens, lambda rng, ql: box["kl"], 32, 8, 128, 16, "bf16",
+                           causal=True, spare=0.1, name="mixed_decode_chunked_prefill_bf16",
+                           values=values)
     raise ValueError(f"no workload {c}")

@@ -87,3 +87,12 @@ def test_varlen_mixed_decode_and_chunked_prefill(dtype):
     kl = [1500, 7, 900, 900, 333, 64]
     case = wl.varlen_case(950, ql, kl, 32, 8, 128, 16, dtype, causal=True)
     check_varlen(case)
+
+
+def test_mixed_batch_named_workload():
+    """24 decode rows, 6 four-token decodes and 2 chunked prefills (512 new
+    queries over 1536 cached keys) in one call, bs 16: every query row of
+    four heads (one per kv-head pair) checked."""
+    case = wl.workload(6)
+    rows = [(r, h) for r in range(case.q.shape[0]) for h in (0, 7, 18, 31)]
+    check_varlen(case, rows=rows)

@@ -399,3 +399,17 @@ def test_generator_slots_follow_the_address_translation():
             for p in range(n):
                 assert case.slot_mapping[t] == oracle.slot_of(case.block_table, b, p, case.block_size)
                 t += 1
+
+
+def test_mixed_workload_shape():
+    """The mixed batch: 24 single-token and 6 four-token decodes over contexts
+    in [512, 4096], then two 512-query chunks over 2048 keys (1536 cached)."""
+    m = wl.workload(6, values=False)
+    ql = np.diff(m.cu_seqlens_q).tolist()
+    assert ql == [1] * 24 + [4] * 6 + [512, 512]
+    kl = m.seq_lens.tolist()
+    assert all(512 <= n <= 4096 for n in kl[:30]) and kl[30:] == [2048, 2048]
+    assert m.block_size == 16 and (m.num_q_heads, m.num_kv_heads, m.head_dim) == (32, 8, 128)
+    # every query is the last Lq positions of its sequence (bottom-right causal)
+    for b in range(m.num_seqs):
+        assert ql[b] <= kl[b]
