@@ -252,6 +252,29 @@ def main():
                              "bytes": m.decode_bytes()}
             del tt
             torch.cuda.empty_cache()
+        # int8 cache on the LLaMA-7B shape: the same decode over 1-byte codes
+        # (per-kv-head scales), fp16 q/out; algorithmic bytes count the codes
+        m = wl.workload(2, values=False)
+        ks, vs = wl.int8_scales(m.num_kv_heads)
+        k8 = torch.randint(-127, 128, m.pool_shape(), dtype=torch.int8, device=dev)
+        v8 = torch.randint_like(k8, -127, 128)
+        q8 = torch.randn(m.num_seqs, m.num_q_heads, m.head_dim, dtype=tdt(m.dtype), device=dev)
+        o8 = torch.empty_like(q8)
+        ksd, vsd = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+        bt8, ctx8 = ints(m.block_table), ints(m.seq_lens)
+        ws8 = torch.empty(max(1, binding.paged_attention_decode_workspace_size(
+            m.num_seqs, m.num_q_heads, m.head_dim, m.max_blocks_per_seq, m.block_size)),
+            dtype=torch.uint8, device=dev)
+        ms = time_calls(lambda: binding.paged_attention_decode_int8(
+            o8, q8, k8, v8, ksd, vsd, bt8, ctx8, m.block_size, m.scale, workspace=ws8), n_extra)
+        mu = statistics.mean(ms)
+        b8 = m.decode_bytes() - m.kv_bytes_read() // 2
+        gbs = b8 / (mu * 1e-3) / 1e9
+        extra["int8_kv_decode_llama7b_b8_ctx2048"] = {
+            "us": round(mu * 1e3, 2), "gbs": round(gbs, 1),
+            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b8}
+        del k8, v8
+        torch.cuda.empty_cache()
         for c in (4, 6):
             # 4: packed causal prefill; 6: decode + multi-token decode + chunked
             # prefill rows in one packed call (its KV GB/s is reported as well)

@@ -165,6 +165,57 @@ int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q
                            int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
                            void* stream);
 
+/*
+ * Int8 KV cache
+ * -------------
+ * The skill page lists int8 KV-cache quantisation among the ways to shrink
+ * the cache (its further-techniques list: "INT8 / W8A8C8"; its FA parameter
+ * table: antiquant_scale, dequant_scale_key / dequant_scale_value). The pages
+ * fix neither the granularity nor the rounding; these calls take the plainest
+ * reading: symmetric codes, one float32 scale per kv head for K and another
+ * for V, value = code * scale.
+ *
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim] int8
+ *   k_scale, v_scale : [num_kv_heads] float32 (device), positive
+ */
+
+/*
+ * paged_kv_write_int8 -- quantise new K/V rows and scatter them by slot.
+ *
+ * For every t < num_tokens with s = slot_mapping[t] in [0, num_blocks *
+ * block_size), element x of kv head h of key[t] becomes
+ *     code = clamp(rne(x / k_scale[h]), -127, 127)
+ * in k_cache row s (rne: round half to even; the quotient is an IEEE
+ * binary32 division of x widened to binary32); value[t] likewise with
+ * v_scale. Slot rules as paged_kv_write (skill page, sections 3.1 and 3.3).
+ * A NaN input gives an unspecified code.
+ *
+ *   key, value : [num_tokens, num_kv_heads, head_dim], dtype (F32, F16, BF16)
+ *   slot_mapping : [num_tokens] int32
+ */
+int paged_kv_write_int8(void* k_cache, void* v_cache, const void* key, const void* value,
+                        const float* k_scale, const float* v_scale, const int32_t* slot_mapping,
+                        int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * paged_attention_decode_int8 -- paged_attention_decode over an int8 cache:
+ * key j of kv head h is k_scale[h] * k_cache code, value j likewise with
+ * v_scale; the attention itself is the one paged_attention_decode defines
+ * (skill page Appendix C, sparse_mode 0; split-KV partitions merged exactly).
+ * q and out are fp16 or bf16 (dtype); the workspace rule is
+ * paged_attention_decode_workspace_size(), as for paged_attention_decode.
+ * Accumulation is fp32; codes enter the matrix cores exactly, the scales are
+ * applied to the scores and to the output in fp32.
+ */
+int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                int32_t block_size, float scale, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a pkv_status value. Never NULL. */
 const char* pkv_status_string(int status);
 

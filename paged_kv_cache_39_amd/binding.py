@@ -63,6 +63,13 @@ def lib() -> ctypes.CDLL:
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pkv_decode_partition_tokens.restype = i32
+        L.paged_kv_write_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64,
+                                          i32, vp]
+        L.paged_kv_write_int8.restype = ctypes.c_int
+        L.paged_attention_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                  ctypes.c_float, i32, i32, i32, i32, i32, i64,
+                                                  i32, vp, sz, vp]
+        L.paged_attention_decode_int8.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -198,6 +205,65 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
         _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), 1 if causal else 0, nseq, total_q, hq, hkv, d, bs, block_table.shape[1],
         nb, _code(q), _stream(stream)))
+
+
+def _int8_pool(k_cache, v_cache, k_scale, v_scale):
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t, torch.int8)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    for n, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _need_gpu(n, t, torch.float32)
+        if t.shape != (hkv,):
+            raise ValueError(f"{n} must be [num_kv_heads] float32")
+    return nb, bs, hkv, d
+
+
+def paged_kv_write_int8(k_cache, v_cache, key, value, k_scale, v_scale, slot_mapping,
+                        stream=None):
+    """Quantise key[t] / value[t] with the per-kv-head scales and store the
+    int8 codes at pool row slot_mapping[t] (skipped if < 0)."""
+    nb, bs, hkv, d = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    for n, t in (("key", key), ("value", value)):
+        _need_gpu(n, t)
+    _need_gpu("slot_mapping", slot_mapping, torch.int32)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, Hkv, D] matching the pool")
+    if key.dtype != value.dtype:
+        raise TypeError("key and value must share a dtype")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping must be [num_tokens]")
+    _check("paged_kv_write_int8", lib().paged_kv_write_int8(
+        _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), key.shape[0], hkv, d, bs, nb, _code(key), _stream(stream)))
+
+
+def paged_attention_decode_int8(out, q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                context_lens, block_size, scale, workspace=None, stream=None):
+    """Single-token paged decode over an int8 cache; q/out fp16 or bf16."""
+    nb, bs, hkv, d = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    for n, t in (("out", out), ("q", q)):
+        _need_gpu(n, t)
+    _need_gpu("block_table", block_table, torch.int32)
+    _need_gpu("context_lens", context_lens, torch.int32)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q/out must be [num_seqs, Hq, D] of one dtype")
+    bsz, hq, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_decode_workspace_size(bsz, hq, d, maxblk, bs) if bsz else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    elif need:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_decode_int8", lib().paged_attention_decode_int8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(context_lens), bs, float(scale), bsz, hq, hkv, d, maxblk, nb,
+        _code(q), _ptr(workspace), ws_bytes, _stream(s)))
 
 
 def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,

@@ -227,17 +227,24 @@ struct MfLds {
   static constexpr int bytes = totalB > mergeB ? totalB : mergeB;
 };
 
-template <class Ty, int D, int WAVES, int TT, int PD>
+// Q8: the cache holds int8 codes with per-kv-head scales (value = code *
+// scale). A 16-byte load then carries 16 codes; they are widened exactly to
+// Ty on the way into LDS, k_scale folds into the score scale and v_scale
+// into the merged output, and everything between is the 16-bit path.
+template <class Ty, int D, int WAVES, int TT, int PD, bool Q8>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, float scale_log2, int num_q_heads,
     int num_kv_heads, int group, int heads_per_wg, int log2_bs, int max_blocks_per_seq,
-    int64_t num_blocks, int num_parts, int part_tokens) {
+    int64_t num_blocks, int num_parts, int part_tokens, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
   using L = MfLds<D, WAVES, TT>;
   constexpr int NT = WAVES * kWave;
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int EB = Q8 ? 1 : 2;      // bytes per cached element
+  constexpr int EPC = 16 / EB;        // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;        // 16-byte chunks per cached row
   constexpr int RPI = kWave / CPR;    // rows per load instruction
   constexpr int LPI = TT / RPI;       // load instructions per tile
   constexpr int KS = D / 32;          // k-steps of q.k
@@ -286,7 +293,11 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   __syncthreads();
 
   const int row_stride = num_kv_heads * D;
-  const int head_off = kvh * D + lch * 8;
+  const int head_off = kvh * D + lch * EPC;
+  const uint8_t* kbytes = static_cast<const uint8_t*>(k_cache);
+  const uint8_t* vbytes = static_cast<const uint8_t*>(v_cache);
+  const float sl2 = Q8 ? scale_log2 * k_scale[kvh] : scale_log2;   // scores in log2 units
+  const float vsc = Q8 ? v_scale[kvh] : 1.f;
   // waves own contiguous, TT-aligned shares of the partition
   const int share = ((ntok + WAVES * TT - 1) / (WAVES * TT)) * TT;
   const int wtok0 = wave * share;
@@ -306,9 +317,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       const int tg = min(t0, last_grp);                    // groups past the end re-read the last
       const int tok = min(tg + lrow, ntok - 1);
       const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
-      const size_t off = ((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off;
-      kk[j] = load16<true>(k_cache + off);
-      vv[j] = load16<true>(v_cache + off);
+      const size_t off = (((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off) * EB;
+      kk[j] = load16<true>(kbytes + off);
+      vv[j] = load16<true>(vbytes + off);
     }
   };
 
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     for (int n = 0; n < NS; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[n][i] = (tbase + 16 * n + i < ntok) ? st[n][i] * scale_log2 : -INFINITY;
+        sv[n][i] = (tbase + 16 * n + i < ntok) ? st[n][i] * sl2 : -INFINITY;
         mx = fmaxf(mx, sv[n][i]);
       }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -391,8 +402,20 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       if (it < niter) {
 #pragma unroll
         for (int j = 0; j < LPI; ++j) {
-          *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 16) = kr[u][j];
-          *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 16) = vr[u][j];
+          uint8_t* dk = s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+          uint8_t* dv = s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+          if constexpr (Q8) {
+            u32x4_t lo, hi;
+            widen_i8x16<Ty>(kr[u][j], lo, hi);
+            *reinterpret_cast<u32x4_t*>(dk) = lo;
+            *reinterpret_cast<u32x4_t*>(dk + 16) = hi;
+            widen_i8x16<Ty>(vr[u][j], lo, hi);
+            *reinterpret_cast<u32x4_t*>(dv) = lo;
+            *reinterpret_cast<u32x4_t*>(dv + 16) = hi;
+          } else {
+            *reinterpret_cast<u32x4_t*>(dk) = kr[u][j];
+            *reinterpret_cast<u32x4_t*>(dv) = vr[u][j];
+          }
         }
         if (it + PD < niter) fetch(it + PD, kr[u], vr[u]);
         tile(it);
@@ -432,6 +455,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       a += s_o[(w * 16 + hh) * L::oRow + d] * wt;
     }
     const size_t bh = (size_t)b * num_q_heads + h0 + hh;
+    a *= vsc;
     if (nparts_b == 1) {
       out[bh * D + d] = from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
     } else {
@@ -542,7 +566,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
 }
 
-template <class Ty, int D, int WAVES, int TT, int PD>
+template <class Ty, int D, int WAVES, int TT, int PD, bool Q8>
 static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
                                   int part_tokens) {
   const int log2_bs = __builtin_ctz(a.block_size);
@@ -550,18 +574,18 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD>), grid, dim3(WAVES * kWave), 0, stream,
-                     static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k_cache),
-                     static_cast<const uint16_t*>(a.v_cache), a.block_table, a.context_lens,
-                     a.ws_ml, a.ws_o, scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw,
-                     log2_bs, a.max_blocks_per_seq, a.num_blocks, parts, part_tokens);
+  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8>), grid, dim3(WAVES * kWave), 0,
+                     stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
+                     a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
+                     scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw, log2_bs,
+                     a.max_blocks_per_seq, a.num_blocks, parts, part_tokens, a.k_scale,
+                     a.v_scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || parts <= 1) return err;
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
 }
 
-template <class Ty, int D>
+template <class Ty, int D, bool Q8 = false>
 static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   int hpw = 1;  // largest divisor of the group size that fits one 16-row tile
@@ -569,8 +593,9 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
     if (group % c == 0) { hpw = c; break; }
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
                                       a.block_size);
-  if (plan.waves == 8) return launch_mfma_cfg<Ty, D, 8, 32, 1>(a, stream, hpw, plan.part_tokens);
-  return launch_mfma_cfg<Ty, D, 4, 16, 1>(a, stream, hpw, plan.part_tokens);
+  if (plan.waves == 8)
+    return launch_mfma_cfg<Ty, D, 8, 32, 1, Q8>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16, 1, Q8>(a, stream, hpw, plan.part_tokens);
 }
 
 template <int D>
@@ -591,6 +616,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     default: return d64 ? launch_decode_mfma<BF16, 64>(a, stream)
                         : launch_decode_mfma<BF16, 128>(a, stream);
   }
+}
+
+hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_dim == 64;
+  if (a.dtype == 1)
+    return d64 ? launch_decode_mfma<F16, 64, true>(a, stream)
+               : launch_decode_mfma<F16, 128, true>(a, stream);
+  return d64 ? launch_decode_mfma<BF16, 64, true>(a, stream)
+             : launch_decode_mfma<BF16, 128, true>(a, stream);
 }
 
 }  // namespace pkv

@@ -47,4 +47,80 @@ hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// int8 cache write: quantise, then scatter by slot. Code of element x of kv
+// head h: clamp(rne(x / scale[h]), -127, 127), the quotient an IEEE float32
+// division (the int8 KV-cache entry points in include/pagedkv.h state the
+// reading). One thread per 16 elements of a token row, i.e. 16 codes = one
+// 16-byte store into the pool.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s) {
+  auto q = [s](float x) -> uint32_t {
+    const float r = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.f), 127.f);
+    return (uint32_t)(int32_t)r & 0xFFu;
+  };
+  return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
+}
+
+template <class Ty>
+__device__ __forceinline__ uint4 quantize16(const typename Ty::storage* x, float s) {
+  const Chunk<Ty, 16> c = load_chunk<Ty, 16>(x);
+  uint4 r;
+  r.x = quantize4(c.get(0), c.get(1), c.get(2), c.get(3), s);
+  r.y = quantize4(c.get(4), c.get(5), c.get(6), c.get(7), s);
+  r.z = quantize4(c.get(8), c.get(9), c.get(10), c.get(11), s);
+  r.w = quantize4(c.get(12), c.get(13), c.get(14), c.get(15), s);
+  return r;
+}
+
+template <class Ty>
+__global__ __launch_bounds__(256) void kv_write_int8_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    const typename Ty::storage* __restrict__ key, const typename Ty::storage* __restrict__ value,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ slot_mapping, int64_t num_pieces, int pieces_per_row,
+    int pieces_per_head, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= num_pieces) return;
+  const int64_t t = gid / pieces_per_row;
+  const int piece = (int)(gid - t * pieces_per_row);
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int head = piece / pieces_per_head;
+  const int64_t dst = (int64_t)slot * pieces_per_row + piece;
+  k_cache[dst] = quantize16<Ty>(key + gid * 16, k_scale[head]);
+  v_cache[dst] = quantize16<Ty>(value + gid * 16, v_scale[head]);
+}
+
+hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, const void* value,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* slot_mapping, int64_t num_tokens, int row_elems,
+                                int head_dim, int64_t num_slots, int dtype, hipStream_t stream) {
+  const int pieces_per_row = row_elems / 16;
+  const int pieces_per_head = head_dim / 16;
+  const int64_t num_pieces = num_tokens * pieces_per_row;
+  const int threads = 256;
+  const dim3 grid((unsigned)((num_pieces + threads - 1) / threads));
+  uint4* kc = static_cast<uint4*>(k_cache);
+  uint4* vc = static_cast<uint4*>(v_cache);
+  if (dtype == 0) {
+    hipLaunchKernelGGL(kv_write_int8_kernel<F32>, grid, dim3(threads), 0, stream, kc, vc,
+                       static_cast<const float*>(key), static_cast<const float*>(value), k_scale,
+                       v_scale, slot_mapping, num_pieces, pieces_per_row, pieces_per_head,
+                       num_slots);
+  } else if (dtype == 1) {
+    hipLaunchKernelGGL(kv_write_int8_kernel<F16>, grid, dim3(threads), 0, stream, kc, vc,
+                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                       k_scale, v_scale, slot_mapping, num_pieces, pieces_per_row,
+                       pieces_per_head, num_slots);
+  } else {
+    hipLaunchKernelGGL(kv_write_int8_kernel<BF16>, grid, dim3(threads), 0, stream, kc, vc,
+                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                       k_scale, v_scale, slot_mapping, num_pieces, pieces_per_row,
+                       pieces_per_head, num_slots);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -273,6 +273,22 @@ struct Mma<F16> {
   }
 };
 
+// 16 int8 codes (one 16-byte chunk, byte k = code k) -> the same 16 values
+// as Ty (two 16-byte chunks, 8 values each). Exact: |code| <= 127 has at
+// most 7 significant bits.
+template <class Ty>
+__device__ __forceinline__ void widen_i8x16(const u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = c[w];
+    r[2 * w] = Mma<Ty>::pack((float)(int8_t)(x & 0xFFu), (float)(int8_t)((x >> 8) & 0xFFu));
+    r[2 * w + 1] = Mma<Ty>::pack((float)(int8_t)((x >> 16) & 0xFFu), (float)(int8_t)(x >> 24));
+  }
+  lo = u32x4_t{r[0], r[1], r[2], r[3]};
+  hi = u32x4_t{r[4], r[5], r[6], r[7]};
+}
+
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane i supplies the address of a row R_i of four 16-bit elements; lane
 // 4a+b receives (R_a[b], R_{a+4}[b], R_{a+8}[b], R_{a+12}[b]).

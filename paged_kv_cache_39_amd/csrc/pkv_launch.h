@@ -43,6 +43,11 @@ inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, 
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
                            const int32_t* slot_mapping, int64_t num_tokens, int row_bytes,
                            int64_t num_slots, hipStream_t stream);
+// quantise rows of row_elems elements (dtype 0/1/2) to int8 codes and scatter them
+hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, const void* value,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* slot_mapping, int64_t num_tokens, int row_elems,
+                                int head_dim, int64_t num_slots, int dtype, hipStream_t stream);
 
 struct DecodeArgs {
   void* out;
@@ -58,9 +63,14 @@ struct DecodeArgs {
   int dtype;
   float* ws_ml;   // [B, Hq, P, 2] (max in log2 units, sum), P = parts at 512 tokens
   float* ws_o;    // [B, Hq, P, D] unnormalised partial outputs
+  // int8 cache only: per-kv-head dequantisation scales ([Hkv] fp32)
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// int8 cache (codes), q/out of a.dtype (fp16 or bf16)
+hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
 
 struct VarlenArgs {
   void* out;

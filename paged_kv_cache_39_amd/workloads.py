@@ -208,6 +208,15 @@ def varlen_case(seed, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, bloc
                      scale=1.0 / math.sqrt(head_dim), cu_seqlens_q=cu, causal=causal)
 
 
+def int8_scales(num_kv_heads):
+    """Per-kv-head int8 dequantisation scales for the synthetic N(0,1) data:
+    fixed, distinct per head, clipping the tails beyond about 3 sigma."""
+    h = np.arange(num_kv_heads, dtype=np.float64)
+    k_scale = ((3.0 + 0.25 * (h % 4)) / 127.0).astype(np.float32)
+    v_scale = ((3.25 + 0.125 * (h % 5)) / 127.0).astype(np.float32)
+    return k_scale, v_scale
+
+
 def log_uniform_lengths(rng, n, lo, hi):
     """round(exp(U(ln lo, ln hi))) clipped to [lo, hi]."""
     x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))

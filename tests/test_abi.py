@@ -153,3 +153,38 @@ def test_binding_refuses_cpu_tensors():
         binding.paged_kv_write(k, k, torch.zeros(1, 2, 64, dtype=torch.float16),
                                torch.zeros(1, 2, 64, dtype=torch.float16),
                                torch.zeros(1, dtype=torch.int32))
+
+
+def test_int8_write_validation(L):
+    def w8(**kw):
+        a = dict(k=FAKE, v=FAKE, key=FAKE, value=FAKE, ks=FAKE, vs=FAKE, slots=FAKE, n=4, hkv=2,
+                 d=128, bs=16, nb=8, dtype=1)
+        a.update(kw)
+        return L.paged_kv_write_int8(a["k"], a["v"], a["key"], a["value"], a["ks"], a["vs"],
+                                     a["slots"], a["n"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                     a["dtype"], None)
+    assert w8(dtype=5) == PKV_ERR_DTYPE
+    assert w8(n=-1) == PKV_ERR_SHAPE
+    assert w8(d=96) == PKV_ERR_UNSUPPORTED
+    assert w8(ks=None) == PKV_ERR_NULL
+    assert w8(vs=None) == PKV_ERR_NULL
+    assert w8(n=0, k=None) == PKV_OK
+
+
+def test_int8_decode_validation(L):
+    def d8(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, ctx=FAKE, bs=16,
+                 scale=0.1, b=2, hq=8, hkv=2, d=128, maxblk=64, nb=256, dtype=2, ws=FAKE,
+                 wsb=1 << 30)
+        a.update(kw)
+        return L.paged_attention_decode_int8(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"],
+                                             a["bt"], a["ctx"], a["bs"], a["scale"], a["b"],
+                                             a["hq"], a["hkv"], a["d"], a["maxblk"], a["nb"],
+                                             a["dtype"], a["ws"], a["wsb"], None)
+    assert d8(dtype=0) == PKV_ERR_DTYPE          # q must be fp16 / bf16 (matrix cores)
+    assert d8(hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert d8(ks=None) == PKV_ERR_NULL
+    assert d8(bs=8) == PKV_ERR_UNSUPPORTED
+    need = L.paged_attention_decode_workspace_size(2, 8, 128, 64, 16)
+    assert d8(wsb=need - 1) == PKV_ERR_WORKSPACE
+    assert d8(b=0, q=None) == PKV_OK

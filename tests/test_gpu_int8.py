@@ -1,0 +1,136 @@
+"""GPU parity of the int8 KV cache: paged_kv_write_int8 against the oracle's
+quantiser (bit-exact codes, untouched cells compared too), and
+paged_attention_decode_int8 against the oracle's decode over the exactly
+dequantised cache (fp64). Tolerances are those of the q dtype: 2e-3 (fp16),
+1.5e-2 (bf16) max abs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_39_amd import binding
+from paged_kv_cache_39_amd import workloads as wl
+from tests.gpu_util import ATOL, ints, max_abs_err, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -128   # never a code: marks cells the write must not touch
+
+
+class Int8Case:
+    def __init__(self, case):
+        self.case = case
+        ks, vs = wl.int8_scales(case.num_kv_heads)
+        self.ks_h, self.vs_h = ks, vs
+        self.k_scale = torch.from_numpy(ks).cuda()
+        self.v_scale = torch.from_numpy(vs).cuda()
+        shape = case.pool_shape()
+        self.k_cache = torch.full(shape, SENTINEL, dtype=torch.int8, device="cuda")
+        self.v_cache = torch.full(shape, SENTINEL, dtype=torch.int8, device="cuda")
+        self.key = to_device(case.key, case.dtype)
+        self.value = to_device(case.value, case.dtype)
+        self.slots = ints(case.slot_mapping)
+        binding.paged_kv_write_int8(self.k_cache, self.v_cache, self.key, self.value,
+                                    self.k_scale, self.v_scale, self.slots)
+
+    def host_codes(self):
+        c = self.case
+        pool = np.full(c.pool_shape(), SENTINEL, np.int8)
+        return oracle.write_kv_int8(pool, pool, c.key, c.value, self.ks_h, self.vs_h,
+                                    c.slot_mapping, c.block_size, c.dtype)
+
+    def decode(self, out=None):
+        c = self.case
+        q = to_device(c.q, c.dtype)
+        out = torch.empty_like(q) if out is None else out
+        binding.paged_attention_decode_int8(out, q, self.k_cache, self.v_cache, self.k_scale,
+                                            self.v_scale, ints(c.block_table), ints(c.seq_lens),
+                                            c.block_size, c.scale)
+        return out
+
+
+def check_write(ic):
+    print(f"int8 write parity: {ic.case.name} dtype={ic.case.dtype}", flush=True)
+    kh, vh = ic.host_codes()
+    assert np.array_equal(ic.k_cache.cpu().numpy(), kh)
+    assert np.array_equal(ic.v_cache.cpu().numpy(), vh)
+    return kh, vh
+
+
+def check_decode(ic, pairs=None):
+    c = ic.case
+    print(f"int8 decode parity: {c.name} dtype={c.dtype} ctx={c.seq_lens.tolist()[:8]} "
+          f"Hq={c.num_q_heads} Hkv={c.num_kv_heads} D={c.head_dim} bs={c.block_size}", flush=True)
+    kh, vh = check_write(ic)
+    got = to_host(ic.decode(), c.dtype)
+    want = oracle.decode_int8(c.q, kh, vh, ic.ks_h, ic.vs_h, c.block_table, c.seq_lens,
+                              c.block_size, c.scale, c.dtype, pairs=pairs)
+    mask = None
+    if pairs is not None:
+        mask = np.zeros(want.shape, dtype=bool)
+        for b, h in pairs:
+            mask[b, h] = True
+    err = max_abs_err(got, want, c.dtype, mask)
+    assert err <= ATOL[c.dtype], f"max abs err {err} > {ATOL[c.dtype]}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_int8_write_bit_exact(dtype):
+    """Every input dtype quantises to the oracle's codes; negative slots skip."""
+    case = wl.decode_case(31, [5, 40, 17], 8, 4, 128, 16, dtype, spare=0.5)
+    case.slot_mapping[3] = -1
+    ic = Int8Case(case)
+    check_write(ic)
+
+
+def test_int8_write_ties_and_clamp():
+    """Values on rounding ties and beyond the clamp, written through the GPU."""
+    case = wl.decode_case(32, [16], 2, 2, 64, 16, "f16")
+    ks, vs = wl.int8_scales(2)
+    steps = np.array([0.5, 1.5, 2.5, -2.5, 126.5, 127.6, 300.0, -300.0], np.float64)
+    vals = np.resize(steps, case.key.shape) * ks.astype(np.float64)[None, :, None]
+    case.key = vals.astype(np.float16)
+    case.value = (np.resize(steps, case.value.shape) * vs.astype(np.float64)[None, :, None]
+                  ).astype(np.float16)
+    check_write(Int8Case(case))
+
+
+EDGE_LENS = [0, 1, 15, 16, 17, 33, 511, 512, 513, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (16, 2), (6, 2)])
+def test_int8_decode_sweep(dtype, d, hq, hkv):
+    bs = {64: 16, 128: 32}[d]
+    case = wl.decode_case(600 + d + hq, EDGE_LENS, hq, hkv, d, bs, dtype, spare=0.25)
+    check_decode(Int8Case(case))
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_int8_decode_block_sizes(bs):
+    case = wl.decode_case(650 + bs, [bs - 1, bs, bs + 1, 700, 1537], 8, 2, 128, bs, "bf16")
+    check_decode(Int8Case(case))
+
+
+def test_int8_decode_whole_context_plan():
+    """>= 256 (sequence, head) rows with contexts <= 2048 (one 8-wave
+    workgroup per context)."""
+    lens = [0, 1, 31, 32, 33, 255, 256, 257, 1023, 1024, 2047, 2048, 1500, 700, 9, 64]
+    case = wl.decode_case(660, lens, 32, 16, 128, 16, "f16", spare=0.2)
+    check_decode(Int8Case(case))
+
+
+def test_int8_llama7b_shaped_full_size():
+    """Batch 8 x 2048, 32/32 heads, D 128, fp16 q, int8 cache: every output."""
+    m = wl.workload(2)
+    check_decode(Int8Case(m))
+
+
+def test_int8_long_context_sampled():
+    """Batch 2 x 65536, 64/8 heads, bs 128: split partitions + reduce."""
+    case = wl.decode_case(670, [65536, 40000], 64, 8, 128, 128, "bf16", spare=0.05)
+    rng = np.random.default_rng(1)
+    pairs = [(b, int(h)) for b in range(2) for h in rng.choice(64, size=6, replace=False)]
+    check_decode(Int8Case(case), pairs=pairs)
