@@ -22,3 +22,4 @@ from .int8_kv import (  # noqa: F401
     quantize_int8,
     write_kv_int8,
 )
+from .block_manager import BlockManager, copy_blocks  # noqa: F401
