@@ -301,6 +301,43 @@ def main():
                 result["prefill_tflops"] = extra[m.name]["tflops"]
             del k, v, q, out
             torch.cuda.empty_cache()
+        # block manager: host cost of one decode step's scheduling (256
+        # sequences at 1024 tokens, bs 16: append one token each, build the
+        # block table and lengths, take the copies), and the device block copy
+        import numpy as np
+        nseq, bsz = 256, 16
+        bm = binding.BlockManager(nseq * (1024 // bsz + 8), bsz)
+        for sq in range(nseq):
+            bm.add_sequence(sq)
+            bm.append(sq, 1024)
+        slots = np.empty(nseq, np.int32)
+        ids = np.arange(nseq, dtype=np.int64)
+        n_host = 200
+        t0 = time.perf_counter()
+        for _ in range(n_host):
+            bm.append_each(ids, 1, slots)
+            bm.block_table(ids, 1024 // bsz + 8)
+            bm.take_copies()
+        host_us = (time.perf_counter() - t0) / n_host * 1e6
+        bm.close()
+        m = wl.workload(2, values=False)
+        kc = torch.randn(m.pool_shape(), dtype=tdt(m.dtype), device=dev)
+        vc = torch.randn_like(kc)
+        npairs = 1024
+        perm = torch.randperm(m.num_blocks)
+        pairs = torch.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).to(torch.int32).to(dev)
+        ms = time_calls(lambda: binding.paged_kv_copy_blocks(kc, vc, pairs), n_extra)
+        mu = statistics.mean(ms)
+        cbytes = 2 * 2 * npairs * m.block_size * m.num_kv_heads * m.head_dim * 2 + npairs * 8
+        extra["block_manager_decode_step_b256"] = {
+            "host_us_per_step": round(host_us, 2),
+            "note": "pkv_bm_append_each (1 token for each of 256 sequences) + block_table + "
+                    "take_copies, one host thread, through the Python binding"}
+        extra["copy_blocks_fp16_1024_blocks"] = {
+            "us": round(mu * 1e3, 2), "gbs": round(cbytes / (mu * 1e-3) / 1e9, 1),
+            "hbm_peak_frac": round(cbytes / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": cbytes}
+        del kc, vc
+        torch.cuda.empty_cache()
         result["other_workloads"] = extra
 
     if not args.no_cpu_baseline:

@@ -53,7 +53,8 @@ extern "C" {
 typedef enum {
   PKV_F32 = 0,  /* IEEE binary32 */
   PKV_F16 = 1,  /* IEEE binary16 */
-  PKV_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+  PKV_BF16 = 2, /* bfloat16 (upper half of a binary32) */
+  PKV_I8 = 3    /* int8 codes (accepted where a call says so) */
 } pkv_dtype;
 
 typedef enum {
@@ -63,7 +64,9 @@ typedef enum {
   PKV_ERR_DTYPE = -3,       /* dtype code unknown or not accepted by this call */
   PKV_ERR_UNSUPPORTED = -4, /* head_dim / block_size outside the supported set */
   PKV_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
-  PKV_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+  PKV_ERR_HIP = -6,         /* the HIP runtime rejected a launch */
+  PKV_ERR_NO_BLOCKS = -7,   /* block manager: not enough free blocks */
+  PKV_ERR_PENDING_COPY = -8 /* block manager: take and apply pending block copies first */
 } pkv_status;
 
 /*
@@ -215,6 +218,25 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole cache blocks: for every pair i,
+ * block pairs[2i+1] of k_cache and of v_cache becomes a copy of block
+ * pairs[2i] (all block_size rows, all kv heads, all dims; bit copy). This is
+ * the device half of copy-on-write (the ATB PagedAttention page: a sequence
+ * that extends a shared page first copies it to a fresh page); the pairs come
+ * from pkv_bm_take_copies() (include/pkv_block_manager.h). The pairs of one
+ * call are copied concurrently: no block may be both a source and a
+ * destination, and no destination may repeat (the block manager guarantees
+ * both). Pairs naming a block outside [0, num_blocks) are skipped.
+ *
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *   pairs            : [num_pairs, 2] int32 (device): (source, destination)
+ *   dtype            : element type of the pool (PKV_F32, PKV_F16, PKV_BF16, PKV_I8)
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, int32_t dtype, void* stream);
 
 /* Static, human-readable text for a pkv_status value. Never NULL. */
 const char* pkv_status_string(int status);

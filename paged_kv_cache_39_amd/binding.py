@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv
 _lib = None
 _lock = threading.Lock()
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8 = 0, 1, 2, 3
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
 
 
@@ -70,6 +70,33 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_float, i32, i32, i32, i32, i32, i64,
                                                   i32, vp, sz, vp]
         L.paged_attention_decode_int8.restype = ctypes.c_int
+        L.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
+        L.paged_kv_copy_blocks.restype = ctypes.c_int
+        L.pkv_bm_create.argtypes = [i64, i32]
+        L.pkv_bm_create.restype = vp
+        L.pkv_bm_destroy.argtypes = [vp]
+        L.pkv_bm_destroy.restype = None
+        for name in ("pkv_bm_add_sequence", "pkv_bm_free_sequence"):
+            getattr(L, name).argtypes = [vp, i64]
+            getattr(L, name).restype = ctypes.c_int
+        L.pkv_bm_fork.argtypes = [vp, i64, i64]
+        L.pkv_bm_fork.restype = ctypes.c_int
+        L.pkv_bm_append.argtypes = [vp, i64, i64, vp]
+        L.pkv_bm_append.restype = ctypes.c_int
+        L.pkv_bm_append_each.argtypes = [vp, vp, i64, i64, vp]
+        L.pkv_bm_append_each.restype = i64
+        L.pkv_bm_num_free_blocks.argtypes = [vp]
+        L.pkv_bm_num_free_blocks.restype = i64
+        L.pkv_bm_sequence_length.argtypes = [vp, i64]
+        L.pkv_bm_sequence_length.restype = i64
+        L.pkv_bm_ref_count.argtypes = [vp, i32]
+        L.pkv_bm_ref_count.restype = i32
+        L.pkv_bm_block_table.argtypes = [vp, vp, i32, i32, vp, vp]
+        L.pkv_bm_block_table.restype = ctypes.c_int
+        L.pkv_bm_num_pending_copies.argtypes = [vp]
+        L.pkv_bm_num_pending_copies.restype = i64
+        L.pkv_bm_take_copies.argtypes = [vp, vp, i64]
+        L.pkv_bm_take_copies.restype = i64
         _lib = L
         return L
 
@@ -264,6 +291,113 @@ def paged_attention_decode_int8(out, q, k_cache, v_cache, k_scale, v_scale, bloc
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_table), _ptr(context_lens), bs, float(scale), bsz, hq, hkv, d, maxblk, nb,
         _code(q), _ptr(workspace), ws_bytes, _stream(s)))
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """Copy block pairs[i, 0] to block pairs[i, 1] in both pools (pairs: int32
+    [n, 2] on the GPU, typically from BlockManager.take_copies())."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    _need_gpu("pairs", pairs, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [num_pairs, 2]")
+    code = PKV_I8 if k_cache.dtype == torch.int8 else _code(k_cache)
+    _check("paged_kv_copy_blocks", lib().paged_kv_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], hkv, d, bs, nb, code,
+        _stream(stream)))
+
+
+class BlockManager:
+    """Host block manager (include/pkv_block_manager.h). Methods return the
+    library's status codes (0 ok, -2 shape, -7 out of blocks, -8 pending
+    copy) rather than raising: running out of blocks is ordinary control flow
+    for a scheduler."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = lib().pkv_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("invalid block manager sizes")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq: int) -> int:
+        return lib().pkv_bm_add_sequence(self._h, int(seq))
+
+    def fork(self, parent: int, child: int) -> int:
+        return lib().pkv_bm_fork(self._h, int(parent), int(child))
+
+    def append(self, seq: int, n: int):
+        """(status, list of the new tokens' slots)."""
+        n = int(n)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        st = lib().pkv_bm_append(self._h, int(seq), n, buf)
+        return st, (list(buf[:n]) if st == 0 else [])
+
+    def append_into(self, seq: int, n: int, out) -> int:
+        """Append n tokens writing their slots into ``out`` (a contiguous int32
+        numpy array or CPU tensor with room for n)."""
+        ptr = out.ctypes.data if hasattr(out, "ctypes") else out.data_ptr()
+        return lib().pkv_bm_append(self._h, int(seq), int(n), ctypes.c_void_p(ptr))
+
+    def append_each(self, seq_ids, tokens_each: int, out=None):
+        """One step: ``tokens_each`` tokens for each of ``seq_ids`` (int64
+        numpy array), slots into ``out`` (int32 numpy, len(seq_ids) *
+        tokens_each). Returns (number of sequences extended, out)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        if out is None:
+            out = np.empty(len(ids) * int(tokens_each), dtype=np.int32)
+        done = lib().pkv_bm_append_each(self._h, ids.ctypes.data, len(ids), int(tokens_each),
+                                        out.ctypes.data)
+        if done < 0:
+            raise PagedKVError("pkv_bm_append_each", int(done), status_string(int(done)))
+        return int(done), out
+
+    def free_sequence(self, seq: int) -> int:
+        return lib().pkv_bm_free_sequence(self._h, int(seq))
+
+    def num_free(self) -> int:
+        return int(lib().pkv_bm_num_free_blocks(self._h))
+
+    def length(self, seq: int) -> int:
+        return int(lib().pkv_bm_sequence_length(self._h, int(seq)))
+
+    def ref_count(self, block: int) -> int:
+        return int(lib().pkv_bm_ref_count(self._h, int(block)))
+
+    def block_table(self, seqs, max_blocks: int):
+        """(status, table int32 [len(seqs), max_blocks] numpy, lens int32 [len(seqs)])."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        table = np.empty((len(ids), int(max_blocks)), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        st = lib().pkv_bm_block_table(self._h, ids.ctypes.data, len(ids), int(max_blocks),
+                                      table.ctypes.data, lens.ctypes.data)
+        return st, (table if st == 0 else None), (lens if st == 0 else None)
+
+    def num_pending_copies(self) -> int:
+        return int(lib().pkv_bm_num_pending_copies(self._h))
+
+    def take_copies(self):
+        """Every pending (src, dst) copy, in order (an int32 numpy array [n, 2])."""
+        import numpy as np
+        n = self.num_pending_copies()
+        out = np.empty((max(n, 1), 2), dtype=np.int32)
+        got = lib().pkv_bm_take_copies(self._h, out.ctypes.data, n)
+        if got < 0:
+            raise PagedKVError("pkv_bm_take_copies", int(got), status_string(int(got)))
+        return out[:got]
 
 
 def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,

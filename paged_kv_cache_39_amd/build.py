@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "varlen.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "varlen.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 

@@ -42,6 +42,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "head_dim or block_size outside the supported set";
     case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
     case PKV_ERR_HIP: return "the HIP runtime rejected a launch";
+    case PKV_ERR_NO_BLOCKS: return "not enough free cache blocks";
+    case PKV_ERR_PENDING_COPY: return "pending block copies must be taken and applied first";
     default: return "unknown status";
   }
 }
@@ -246,6 +248,25 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   hipError_t err = pkv::launch_decode_int8(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, int32_t dtype, void* stream) {
+  if (!valid_dtype(dtype) && dtype != PKV_I8) return PKV_ERR_DTYPE;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return PKV_ERR_NULL;
+  const int eb = dtype == PKV_I8 ? 1 : elem_bytes(dtype);
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * eb;
+  if (block_bytes / 16 > INT32_MAX) return PKV_ERR_SHAPE;
+  if (num_pairs > INT64_MAX / (block_bytes / 16)) return PKV_ERR_SHAPE;
+  hipError_t err = pkv::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs,
+                                           (int)(block_bytes / 16), num_blocks,
+                                           static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -48,6 +48,43 @@ hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const 
 }
 
 // ---------------------------------------------------------------------------
+// Block copies (the device half of copy-on-write): one thread per 16-byte
+// piece of a block; pair i copies block pairs[2i] to block pairs[2i+1] in
+// both pools. Pairs naming a block outside the pool are skipped.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t num_pieces, int pieces_per_block,
+                                                          int64_t num_blocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= num_pieces) return;
+  const int64_t i = gid / pieces_per_block;
+  const int piece = (int)(gid - i * pieces_per_block);
+  const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t s = (int64_t)src * pieces_per_block + piece;
+  const int64_t d = (int64_t)dst * pieces_per_block + piece;
+  const uint4 kk = k_cache[s];
+  const uint4 vv = v_cache[s];
+  k_cache[d] = kk;
+  v_cache[d] = vv;
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                              int64_t num_pairs, int pieces_per_block, int64_t num_blocks,
+                              hipStream_t stream) {
+  const int64_t num_pieces = num_pairs * pieces_per_block;
+  const int threads = 256;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((num_pieces + threads - 1) / threads)),
+                     dim3(threads), 0, stream, static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), pairs, num_pieces, pieces_per_block,
+                     num_blocks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // int8 cache write: quantise, then scatter by slot. Code of element x of kv
 // head h: clamp(rne(x / scale[h]), -127, 127), the quotient an IEEE float32
 // division (the int8 KV-cache entry points in include/pagedkv.h state the

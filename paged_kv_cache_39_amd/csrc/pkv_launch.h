@@ -43,6 +43,10 @@ inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, 
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,
                            const int32_t* slot_mapping, int64_t num_tokens, int row_bytes,
                            int64_t num_slots, hipStream_t stream);
+// whole-block copies: pieces_per_block 16-byte pieces per block, pairs [n, 2] (src, dst)
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                              int64_t num_pairs, int pieces_per_block, int64_t num_blocks,
+                              hipStream_t stream);
 // quantise rows of row_elems elements (dtype 0/1/2) to int8 codes and scatter them
 hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, const void* value,
                                 const float* k_scale, const float* v_scale,

@@ -18,7 +18,8 @@ PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = -4, -5, -6
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    import glob
+    text = "\n".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = binding.status_string(st)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"
@@ -188,3 +189,21 @@ def test_int8_decode_validation(L):
     need = L.paged_attention_decode_workspace_size(2, 8, 128, 64, 16)
     assert d8(wsb=need - 1) == PKV_ERR_WORKSPACE
     assert d8(b=0, q=None) == PKV_OK
+
+
+def test_copy_blocks_validation(L):
+    def cp(**kw):
+        a = dict(k=FAKE, v=FAKE, pairs=FAKE, n=3, hkv=2, d=128, bs=16, nb=8, dtype=3)
+        a.update(kw)
+        return L.paged_kv_copy_blocks(a["k"], a["v"], a["pairs"], a["n"], a["hkv"], a["d"],
+                                      a["bs"], a["nb"], a["dtype"], None)
+    assert cp(dtype=4) == PKV_ERR_DTYPE
+    assert cp(n=-1) == PKV_ERR_SHAPE
+    assert cp(bs=8) == PKV_ERR_UNSUPPORTED
+    assert cp(pairs=None) == PKV_ERR_NULL
+    assert cp(n=0, k=None) == PKV_OK
+
+
+def test_block_manager_exports(L):
+    for name in ("pkv_bm_create", "pkv_bm_append", "pkv_bm_take_copies", "pkv_bm_block_table"):
+        assert name in declared_functions() and hasattr(L, name)
