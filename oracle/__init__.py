@@ -23,3 +23,4 @@ from .int8_kv import (  # noqa: F401
     write_kv_int8,
 )
 from .block_manager import BlockManager, copy_blocks  # noqa: F401
+from .variants import attend, decode_ext, varlen_ext  # noqa: F401

@@ -217,6 +217,13 @@ def int8_scales(num_kv_heads):
     return k_scale, v_scale
 
 
+def alibi_slopes(num_heads):
+    """ALiBi slopes for the synthetic runs: 2^(-8 (h + 1) / H), the geometric
+    sequence of the ALiBi paper for a power-of-two head count."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / num_heads) for h in range(num_heads)],
+                    dtype=np.float32)
+
+
 def log_uniform_lengths(rng, n, lo, hi):
     """round(exp(U(ln lo, ln hi))) clipped to [lo, hi]."""
     x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))
