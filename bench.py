@@ -301,6 +301,47 @@ def main():
                 result["prefill_tflops"] = extra[m.name]["tflops"]
             del k, v, q, out
             torch.cuda.empty_cache()
+        # variants: ALiBi + a sliding window. Decode on the LLaMA-7B shape
+        # (window 1024: bytes = the visible keys' rows), packed prefill of
+        # workload 4 (window 512: flops = allowed pairs)
+        m = wl.workload(2, values=False)
+        tt = decode_setup(m)
+        slopes = torch.from_numpy(wl.alibi_slopes(m.num_q_heads)).to(dev)
+        win = 1024
+        ms = time_calls(lambda: binding.paged_attention_decode_ex(
+            tt["out"], tt["q"], tt["k"], tt["v"], tt["bt"], tt["ctx"], m.block_size, m.scale,
+            slopes, win, workspace=tt["ws"]), n_extra)
+        mu = statistics.mean(ms)
+        vis = sum(min(int(n), win + 1) for n in m.seq_lens)
+        eb = 2
+        bw = vis * 2 * m.num_kv_heads * m.head_dim * eb + 2 * m.num_seqs * m.num_q_heads * m.head_dim * eb
+        extra["decode_alibi_window1024_llama7b"] = {
+            "us": round(mu * 1e3, 2), "gbs": round(bw / (mu * 1e-3) / 1e9, 1),
+            "hbm_peak_frac": round(bw / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": bw}
+        del tt
+        torch.cuda.empty_cache()
+        m = wl.workload(4, values=False)
+        dtp = tdt(m.dtype)
+        k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
+        v = torch.randn_like(k)
+        q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp, device=dev)
+        out = torch.empty_like(q)
+        cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
+        slopes = torch.from_numpy(wl.alibi_slopes(m.num_q_heads)).to(dev)
+        win = 512
+        ms = time_calls(lambda: binding.paged_attention_varlen_ex(
+            out, q, cu, k, v, bt, sl, True, slopes, win), n_extra)
+        mu = statistics.mean(ms)
+        pairs = 0
+        for b in range(m.num_seqs):
+            lq = int(m.cu_seqlens_q[b + 1] - m.cu_seqlens_q[b])
+            pairs += sum(min(i, win) + 1 for i in range(lq))      # Lq == Lk here
+        fl = 4 * m.head_dim * m.num_q_heads * pairs
+        extra["prefill_alibi_window512_16seq"] = {
+            "us": round(mu * 1e3, 2), "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
+            "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops": fl}
+        del k, v, q, out
+        torch.cuda.empty_cache()
         # block manager: host cost of one decode step's scheduling (256
         # sequences at 1024 tokens, bs 16: append one token each, build the
         # block table and lengths, take the copies), and the device block copy

@@ -169,6 +169,43 @@ int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q
                            void* stream);
 
 /*
+ * Attention variants: sliding window and ALiBi
+ * --------------------------------------------
+ * The skill page's FA mask modes include "Band" (a sliding window, used for
+ * prefill and decode of sliding-window models, given a count of preceding
+ * tokens), and the FA call on the cann-recipes-infer page takes alibi_slopes
+ * for ALiBi positional encoding. Readings: positions are aligned to the last
+ * key as for the causal mask (local query i of a sequence with Lq queries and
+ * Lk keys sits at p = i + Lk - Lq; a decode query at p = Lk - 1);
+ *   window_left >= 0 : the query sees keys j >= p - window_left (itself and
+ *                      window_left keys before it); negative: no window;
+ *   alibi_slopes     : NULL, or [num_q_heads] float32 (device); query head h
+ *                      adds alibi_slopes[h] * (j - p) to the scaled score.
+ * A query with no visible key outputs zeros.
+ */
+
+/* paged_attention_decode with the variants above; q/out fp16 or bf16. Other
+ * arguments and the workspace rule are those of paged_attention_decode. */
+int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              int32_t block_size, float scale, const float* alibi_slopes,
+                              int32_t window_left, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* paged_attention_varlen with the variants above (window and ALiBi; the
+ * window bounds keys below the query, and with causal == 0 keys after it
+ * stay visible). Other arguments as paged_attention_varlen. */
+int paged_attention_varlen_ex(void* out, const void* q, const int32_t* cu_seqlens_q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int causal,
+                              const float* alibi_slopes, int32_t window_left, int32_t num_seqs,
+                              int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
  * Int8 KV cache
  * -------------
  * The skill page lists int8 KV-cache quantisation among the ways to shrink

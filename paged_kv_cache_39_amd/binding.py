@@ -70,6 +70,14 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_float, i32, i32, i32, i32, i32, i64,
                                                   i32, vp, sz, vp]
         L.paged_attention_decode_int8.restype = ctypes.c_int
+        L.paged_attention_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                                i32, i32, i32, i32, i32, i32, i64, i32, vp, sz,
+                                                vp]
+        L.paged_attention_decode_ex.restype = ctypes.c_int
+        L.paged_attention_varlen_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                                i32, i32, i64, i32, i32, i32, i32, i32, i64, i32,
+                                                vp]
+        L.paged_attention_varlen_ex.restype = ctypes.c_int
         L.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
         L.paged_kv_copy_blocks.restype = ctypes.c_int
         L.pkv_bm_create.argtypes = [i64, i32]
@@ -232,6 +240,72 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
         _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), 1 if causal else 0, nseq, total_q, hq, hkv, d, bs, block_table.shape[1],
         nb, _code(q), _stream(stream)))
+
+
+def paged_attention_varlen_ex(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
+                              causal=True, alibi_slopes=None, window_left=-1, stream=None):
+    """paged_attention_varlen with ALiBi slopes (float32 [Hq] on the GPU, or
+    None) and a sliding window (negative: none)."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _need_gpu(n, t, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [total_q, Hq, D]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q/out dtype must match the pool")
+    nseq = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (nseq + 1,) or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q must be [num_seqs+1], block_table [num_seqs, max_blocks]")
+    total_q, hq, _ = q.shape
+    if alibi_slopes is not None:
+        _need_gpu("alibi_slopes", alibi_slopes, torch.float32)
+        if alibi_slopes.shape != (hq,):
+            raise ValueError("alibi_slopes must be [num_q_heads]")
+    _check("paged_attention_varlen_ex", lib().paged_attention_varlen_ex(
+        _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), 1 if causal else 0, _ptr(alibi_slopes), int(window_left), nseq, total_q,
+        hq, hkv, d, bs, block_table.shape[1], nb, _code(q), _stream(stream)))
+
+
+def paged_attention_decode_ex(out, q, k_cache, v_cache, block_table, context_lens, block_size,
+                              scale, alibi_slopes=None, window_left=-1, workspace=None,
+                              stream=None):
+    """paged_attention_decode with ALiBi slopes (float32 [Hq] on the GPU, or
+    None) and a sliding window (keys within window_left before the query;
+    negative: none). q/out fp16 or bf16."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    _need_gpu("block_table", block_table, torch.int32)
+    _need_gpu("context_lens", context_lens, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [num_seqs, Hq, D]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q/out dtype must match the pool")
+    bsz, hq, _ = q.shape
+    if alibi_slopes is not None:
+        _need_gpu("alibi_slopes", alibi_slopes, torch.float32)
+        if alibi_slopes.shape != (hq,):
+            raise ValueError("alibi_slopes must be [num_q_heads]")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_decode_workspace_size(bsz, hq, d, maxblk, bs) if bsz else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    elif need:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_decode_ex", lib().paged_attention_decode_ex(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+        bs, float(scale), _ptr(alibi_slopes), int(window_left), bsz, hq, hkv, d, maxblk, nb,
+        _code(q), _ptr(workspace), ws_bytes, _stream(s)))
 
 
 def _int8_pool(k_cache, v_cache, k_scale, v_scale):

@@ -31,6 +31,53 @@ int decode_num_parts(int32_t max_blocks_per_seq, int32_t block_size) {
 
 }  // namespace
 
+static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int causal,
+                           int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                           void* stream, const float* alibi, int32_t window_left, bool ext) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (dtype == PKV_F32) return PKV_ERR_DTYPE;  // matrix-core path: 16-bit inputs only
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 128) return PKV_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (total_q > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
+    return PKV_ERR_NULL;
+
+  pkv::VarlenArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.causal = causal ? 1 : 0;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.dtype = dtype;
+  a.alibi = alibi;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  hipError_t err = ext ? pkv::launch_varlen_ext(a, static_cast<hipStream_t>(stream))
+                       : pkv::launch_varlen(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 extern "C" {
 
 const char* pkv_status_string(int status) {
@@ -145,32 +192,53 @@ int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
                            void* stream) {
-  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
-  if (dtype == PKV_F32) return PKV_ERR_DTYPE;  // matrix-core path: 16-bit inputs only
-  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
-    return PKV_ERR_SHAPE;
+  return varlen_impl(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, causal,
+                     num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, dtype, stream, nullptr, -1, false);
+}
+
+int paged_attention_varlen_ex(void* out, const void* q, const int32_t* cu_seqlens_q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int causal,
+                              const float* alibi_slopes, int32_t window_left, int32_t num_seqs,
+                              int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t dtype, void* stream) {
+  return varlen_impl(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, causal,
+                     num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, dtype, stream, alibi_slopes, window_left,
+                     true);
+}
+
+int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              int32_t block_size, float scale, const float* alibi_slopes,
+                              int32_t window_left, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_DTYPE;  // matrix-core path
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
   int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
   if (st != PKV_OK) return st;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-  if (num_q_heads / num_kv_heads > 128) return PKV_ERR_UNSUPPORTED;
-  if (num_kv_heads > 65535) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
-  if (total_q > INT32_MAX / 2) return PKV_ERR_SHAPE;
-  if (num_seqs == 0 || total_q == 0) return PKV_OK;
-  if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
-    return PKV_ERR_NULL;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                            max_blocks_per_seq, block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
 
-  pkv::VarlenArgs a;
+  pkv::DecodeArgs a;
   a.out = out;
   a.q = q;
-  a.cu_seqlens_q = cu_seqlens_q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.causal = causal ? 1 : 0;
+  a.context_lens = context_lens;
+  a.scale = scale;
   a.num_seqs = num_seqs;
-  a.total_q = total_q;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
@@ -178,7 +246,13 @@ int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  hipError_t err = pkv::launch_varlen(a, static_cast<hipStream_t>(stream));
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
+                                                                          block_size);
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  a.alibi = alibi_slopes;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  hipError_t err = pkv::launch_decode_ext(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -231,7 +231,11 @@ struct MfLds {
 // scale). A 16-byte load then carries 16 codes; they are widened exactly to
 // Ty on the way into LDS, k_scale folds into the score scale and v_scale
 // into the merged output, and everything between is the 16-bit path.
-template <class Ty, int D, int WAVES, int TT, int PD, bool Q8>
+// EXT: the attention variants -- a sliding window (keys j >= ctx-1-window_left
+// only, window_left >= 0) and ALiBi (score + alibi[h] * (j - (ctx-1)));
+// alibi may be NULL and window_left negative. Positions are those of the
+// decode query, the last token of its context.
+template <class Ty, int D, int WAVES, int TT, int PD, bool Q8, bool EXT>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_o, float scale_log2, int num_q_heads,
     int num_kv_heads, int group, int heads_per_wg, int log2_bs, int max_blocks_per_seq,
     int64_t num_blocks, int num_parts, int part_tokens, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale) {
+    const float* __restrict__ v_scale, const float* __restrict__ alibi, int window_left) {
   using L = MfLds<D, WAVES, TT>;
   constexpr int NT = WAVES * kWave;
   constexpr int EB = Q8 ? 1 : 2;      // bytes per cached element
@@ -265,6 +269,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
   int ctx = context_lens[b];
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
+  // visible keys [lo, ctx); loads start at lo16 (16-aligned: one block per load)
+  const int lo = (EXT && window_left >= 0) ? max(0, ctx - 1 - window_left) : 0;
+  const int lo16 = lo & ~15;
   const int part_start = p * part_tokens;
   if (part_start >= ctx) {
     if (p == 0) {
@@ -273,7 +280,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
     return;
   }
+  if (EXT && part_start + part_tokens <= lo16) return;   // no visible key: the reduce skips it
   const int ntok = min(part_tokens, ctx - part_start);
+  const int tb = EXT ? max(0, lo16 - part_start) : 0;    // first local token loaded
   const int nparts_b = (ctx + part_tokens - 1) / part_tokens;
 
   const int nblk = (ntok + bs - 1) >> log2_bs;
@@ -298,9 +307,13 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const uint8_t* vbytes = static_cast<const uint8_t*>(v_cache);
   const float sl2 = Q8 ? scale_log2 * k_scale[kvh] : scale_log2;   // scores in log2 units
   const float vsc = Q8 ? v_scale[kvh] : 1.f;
-  // waves own contiguous, TT-aligned shares of the partition
-  const int share = ((ntok + WAVES * TT - 1) / (WAVES * TT)) * TT;
-  const int wtok0 = wave * share;
+  // ALiBi slope of the lane's head, log2 units
+  const float al2 = (EXT && alibi != nullptr && head_ok) ? alibi[h0 + l16] * 1.4426950408889634f
+                                                         : 0.f;
+  const int lo_local = lo - part_start;
+  // waves own contiguous, TT-aligned shares of [tb, ntok)
+  const int share = ((ntok - tb + WAVES * TT - 1) / (WAVES * TT)) * TT;
+  const int wtok0 = tb + wave * share;
   const int wtok_n = max(0, min(ntok - wtok0, share));
   const int niter = (wtok_n + TT - 1) / TT;
   const int last_grp = (ntok - 1) & ~(RPI - 1);
@@ -345,13 +358,22 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
     // lane holds tokens 16n + 4*g4 + i of this tile for head l16
     const int tbase = wtok0 + it * TT + 4 * g4;
+    // distance of the lane's first token to the query (ALiBi)
+    const float dj0 = (float)(part_start + tbase - (ctx - 1));
     float sv[NS][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < NS; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[n][i] = (tbase + 16 * n + i < ntok) ? st[n][i] * sl2 : -INFINITY;
+        const int t = tbase + 16 * n + i;
+        bool vis = t < ntok;
+        float x = st[n][i] * sl2;
+        if constexpr (EXT) {
+          vis = vis && t >= lo_local;
+          x = fmaf(al2, dj0 + (float)(16 * n + i), x);
+        }
+        sv[n][i] = vis ? x : -INFINITY;
         mx = fmaxf(mx, sv[n][i]);
       }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -477,7 +499,7 @@ template <class Ty, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_reduce_kernel(
     typename Ty::storage* __restrict__ out, const float* __restrict__ ws_ml,
     const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens, int num_q_heads,
-    int log2_bs, int max_blocks_per_seq, int num_parts, int part_tokens) {
+    int log2_bs, int max_blocks_per_seq, int num_parts, int part_tokens, int window_left) {
   constexpr int EPL = D / kWave;
   __shared__ float s_red[kDecWaves];
   __shared__ float s_acc[kDecWaves][D + 1];
@@ -487,12 +509,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_reduce_kernel(
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
   const int np = (ctx + part_tokens - 1) / part_tokens;
   if (np <= 1) return;
+  // with a window, partitions wholly below it wrote nothing (same rule as the
+  // partition kernel)
+  const int p_lo =
+      window_left >= 0 ? ((max(0, ctx - 1 - window_left) & ~15) / part_tokens) : 0;
   const size_t bh = (size_t)b * num_q_heads + h;
   const float* ml = ws_ml + bh * num_parts * 2;
   const float* o = ws_o + bh * num_parts * D;
 
   float mm = -INFINITY;
-  for (int p = tid; p < np; p += kDecThreads) mm = fmaxf(mm, ml[2 * p]);
+  for (int p = p_lo + tid; p < np; p += kDecThreads) mm = fmaxf(mm, ml[2 * p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
   if (lane == 0) s_red[wave] = mm;
@@ -503,7 +529,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_reduce_kernel(
   float a[EPL], ll = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-  int p = wave;
+  int p = p_lo + wave;
   for (; p + 3 * kDecWaves < np; p += 4 * kDecWaves) {
     float w4[4], v4[4][EPL];
 #pragma unroll
@@ -544,7 +570,7 @@ static hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream, int log
   hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(a.num_q_heads, a.num_seqs),
                      dim3(kDecThreads), 0, stream, static_cast<S*>(a.out), a.ws_ml, a.ws_o,
                      a.context_lens, a.num_q_heads, log2_bs, a.max_blocks_per_seq, num_parts,
-                     part_tokens);
+                     part_tokens, a.window_left);
   return hipGetLastError();
 }
 
@@ -566,7 +592,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
 }
 
-template <class Ty, int D, int WAVES, int TT, int PD, bool Q8>
+template <class Ty, int D, int WAVES, int TT, int PD, bool Q8, bool EXT>
 static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
                                   int part_tokens) {
   const int log2_bs = __builtin_ctz(a.block_size);
@@ -574,18 +600,18 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8>), grid, dim3(WAVES * kWave), 0,
+  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
                      stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
                      scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw, log2_bs,
                      a.max_blocks_per_seq, a.num_blocks, parts, part_tokens, a.k_scale,
-                     a.v_scale);
+                     a.v_scale, a.alibi, a.window_left);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || parts <= 1) return err;
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
 }
 
-template <class Ty, int D, bool Q8 = false>
+template <class Ty, int D, bool Q8 = false, bool EXT = false>
 static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   int hpw = 1;  // largest divisor of the group size that fits one 16-row tile
@@ -594,8 +620,8 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
                                       a.block_size);
   if (plan.waves == 8)
-    return launch_mfma_cfg<Ty, D, 8, 32, 1, Q8>(a, stream, hpw, plan.part_tokens);
-  return launch_mfma_cfg<Ty, D, 4, 16, 1, Q8>(a, stream, hpw, plan.part_tokens);
+    return launch_mfma_cfg<Ty, D, 8, 32, 1, Q8, EXT>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16, 1, Q8, EXT>(a, stream, hpw, plan.part_tokens);
 }
 
 template <int D>
@@ -616,6 +642,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     default: return d64 ? launch_decode_mfma<BF16, 64>(a, stream)
                         : launch_decode_mfma<BF16, 128>(a, stream);
   }
+}
+
+hipError_t launch_decode_ext(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_dim == 64;
+  if (a.dtype == 1)
+    return d64 ? launch_decode_mfma<F16, 64, false, true>(a, stream)
+               : launch_decode_mfma<F16, 128, false, true>(a, stream);
+  return d64 ? launch_decode_mfma<BF16, 64, false, true>(a, stream)
+             : launch_decode_mfma<BF16, 128, false, true>(a, stream);
 }
 
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {

@@ -70,9 +70,14 @@ struct DecodeArgs {
   // int8 cache only: per-kv-head dequantisation scales ([Hkv] fp32)
   const float* k_scale = nullptr;
   const float* v_scale = nullptr;
+  // variants: ALiBi slopes [Hq] fp32 (NULL = none), window (negative = none)
+  const float* alibi = nullptr;
+  int window_left = -1;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// window / ALiBi variants, q/out of a.dtype (fp16 or bf16)
+hipError_t launch_decode_ext(const DecodeArgs& a, hipStream_t stream);
 // int8 cache (codes), q/out of a.dtype (fp16 or bf16)
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
 
@@ -90,8 +95,12 @@ struct VarlenArgs {
   int num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int64_t num_blocks;
   int dtype;
+  // variants: ALiBi slopes [Hq] fp32 (NULL = none), window (negative = none)
+  const float* alibi = nullptr;
+  int window_left = -1;
 };
 
 hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream);
+hipError_t launch_varlen_ext(const VarlenArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -127,14 +127,17 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
   return false;
 }
 
-template <class Ty, int D>
+// EXT: the attention variants -- a sliding window (keys j >= p - window_left
+// for the query at p = i + Lk - Lq, window_left >= 0) and ALiBi (score +
+// alibi[h] * (j - p)); alibi may be NULL and window_left negative.
+template <class Ty, int D, bool EXT>
 __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu_seqlens_q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2,
-    int tiles_per_head) {
+    int tiles_per_head, const float* __restrict__ alibi, int window_left) {
   using L = VlLds<D>;
   constexpr int KS = D / 32;                 // k-steps of the QK product
   constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
@@ -220,6 +223,22 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int last_q = min(q0 + bq, lq) - 1;
   const int kv_end = causal ? min(lk, last_q + delta + 1) : lk;
   const int nomask_end = causal ? min(lk, q0 + delta + 1) : lk;
+  // variants: row r's lowest visible key (window) and ALiBi slope (log2
+  // units); the tile starts at its rows' lowest bound, 64-aligned, and keys
+  // below `mask_lo_end` are hidden from some row of the tile
+  const bool windowed = EXT && window_left >= 0;
+  int wlo[2] = {0, 0}, p_abs[2] = {0, 0};
+  float al2[2] = {0.f, 0.f};
+  if constexpr (EXT) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      p_abs[mt] = q_pos[mt] + delta;
+      wlo[mt] = windowed ? max(0, p_abs[mt] - window_left) : 0;
+      al2[mt] = (alibi != nullptr && row_ok[mt]) ? alibi[head[mt]] * 1.4426950408889634f : 0.f;
+    }
+  }
+  const int kv_begin = windowed ? (max(0, q0 + delta - window_left) & ~(kVlBN - 1)) : 0;
+  const int mask_lo_end = windowed ? max(0, last_q + delta - window_left) : 0;
 
   const int row_stride = num_kv_heads * D;
   const int32_t* bt_row = block_table + (size_t)b * max_blocks_per_seq;
@@ -297,7 +316,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
   };
 
-  if (kv_end > 0) stage(0, 0);
+  if (kv_begin < kv_end) stage(0, kv_begin);
 
   // Q^T operands (B of S^T = K Q^T): lane holds Q[row][32s + 8*g4 .. +8]
   u32x4_t qb[2][KS];
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int vchunk = (l16 & 3) >> 1;
 
   int it = 0;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += kVlBN, ++it) {
+  for (int kv0 = kv_begin; kv0 < kv_end; kv0 += kVlBN, ++it) {
     const int cur = it & 1;
     const bool more = kv0 + kVlBN < kv_end;
     if (more) stage(cur ^ 1, kv0 + kVlBN);
@@ -350,7 +369,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     barrier_lds_ops();
     const uint8_t* sk = s_kv + cur * L::stageB;
     const uint8_t* sv = sk + L::tileB;
-    const bool need_mask = kv0 + kVlBN > nomask_end;
+    const bool need_mask = kv0 + kVlBN > nomask_end || (windowed && kv0 < mask_lo_end);
 
     // Operand reads from LDS are issued a phase ahead of the MFMAs that use
     // them, so their latency hides behind the softmax arithmetic:
@@ -405,16 +424,37 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       // positive) and the exponent is one fma, s*scale - m.
       if (need_mask) {
         // key kv0 + 32hh + 16n + 4*g4 + i is visible iff 32hh + 16n + i <= thr
+        // (and, with a window, >= thr_lo)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const int thr = lim[mt] - kv0 - 4 * g4;
+          const int thr_lo = wlo[mt] - kv0 - 4 * g4;
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int o = 32 * hh + 16 * n + i;
+              const bool vis = EXT ? (o <= thr && o >= thr_lo) : (o <= thr);
+              st_cur[n][mt][i] = vis ? st_cur[n][mt][i] : -INFINITY;
+            }
+        }
+      }
+      // variants: scores are scaled and biased here (the max must see the
+      // bias), so the exponent below takes a unit scale
+      if constexpr (EXT) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const float dj0 = (float)(kv0 + 32 * hh + 4 * g4 - p_abs[mt]);
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              st_cur[n][mt][i] = 32 * hh + 16 * n + i <= thr ? st_cur[n][mt][i] : -INFINITY;
+              st_cur[n][mt][i] =
+                  fmaf(st_cur[n][mt][i], scale_log2, al2[mt] * (dj0 + (float)(16 * n + i)));
         }
       }
+      constexpr float one = 1.f;
+      const float sc = EXT ? one : scale_log2;
       // lane-local maxima (raw scores); the row max over the 4 lane groups is
       // only needed when the running max has to move
       // (maximum, not fmax: no NaN canonicalisation of the MFMA results)
@@ -424,7 +464,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         float a = st_cur[0][mt][0];
 #pragma unroll
         for (int k = 1; k < 8; ++k) a = __builtin_elementwise_maximum(a, st_cur[k >> 2][mt][k & 3]);
-        mx[mt] = a * scale_log2;
+        mx[mt] = a * sc;
       }
       const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
@@ -449,7 +489,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], scale_log2, nref[mt]));
+          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], sc, nref[mt]));
         pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
         pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
         pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
@@ -488,30 +528,39 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   }
 }
 
-template <class Ty, int D>
+template <class Ty, int D, bool EXT>
 static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int bq = kVlRows / group;
   const int64_t tiles = (a.total_q + bq - 1) / bq + a.num_seqs;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)a.head_dim);
   dim3 grid((unsigned)(tiles * a.num_kv_heads));
-  hipLaunchKernelGGL((varlen_prefill_kernel<Ty, D>), grid, dim3(kVlThreads), 0, stream,
+  hipLaunchKernelGGL((varlen_prefill_kernel<Ty, D, EXT>), grid, dim3(kVlThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
                      static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens,
                      a.causal, a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
                      __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks,
-                     scale_log2, (int)tiles);
+                     scale_log2, (int)tiles, a.alibi, a.window_left);
   return hipGetLastError();
 }
 
-hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
+template <bool EXT>
+static hipError_t launch_varlen_any(const VarlenArgs& a, hipStream_t stream) {
   if (a.dtype == 1) {
-    return a.head_dim == 64 ? launch_varlen_t<F16, 64>(a, stream)
-                            : launch_varlen_t<F16, 128>(a, stream);
+    return a.head_dim == 64 ? launch_varlen_t<F16, 64, EXT>(a, stream)
+                            : launch_varlen_t<F16, 128, EXT>(a, stream);
   }
-  return a.head_dim == 64 ? launch_varlen_t<BF16, 64>(a, stream)
-                          : launch_varlen_t<BF16, 128>(a, stream);
+  return a.head_dim == 64 ? launch_varlen_t<BF16, 64, EXT>(a, stream)
+                          : launch_varlen_t<BF16, 128, EXT>(a, stream);
+}
+
+hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
+  return launch_varlen_any<false>(a, stream);
+}
+
+hipError_t launch_varlen_ext(const VarlenArgs& a, hipStream_t stream) {
+  return launch_varlen_any<true>(a, stream);
 }
 
 }  // namespace pkv
