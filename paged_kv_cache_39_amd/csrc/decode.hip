@@ -6,9 +6,10 @@
 // Appendix C: decode uses no mask and the KV length bounds the keys; the
 // "ATB PagedAttention" page computes it page by page with an online softmax).
 //
-// Split-KV: the context is cut into partitions of kDecodePart tokens. One
-// workgroup handles one (partition, group of query heads sharing a kv head,
-// sequence) and produces, per query head, the partial triple
+// Split-KV: the context is cut into partitions (kDecodePart tokens here; the
+// matrix-core kernel's launch plan takes 512 to 4096). One workgroup handles
+// one (partition, group of query heads sharing a kv head, sequence) and
+// produces, per query head, the partial triple
 //   m = max score (log2 units), l = sum 2^(s - m), o = sum 2^(s - m) V.
 // A sequence with a single partition is normalised in place; otherwise the
 // reduce kernel merges the triples exactly (the vLLM-on-CANN page: physically
@@ -28,7 +29,7 @@ namespace pkv {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kMaxPartTokens = 2048;   // longest partition a workgroup takes
+constexpr int kMaxPartTokens = kDecodeMaxPart;   // longest partition a workgroup takes
 constexpr int kQuadsPerIter = 8;                  // each row handles 8 tokens per iteration
 constexpr int kTokPerIter = 4 * kQuadsPerIter;    // 32 tokens per wave iteration
 

@@ -22,14 +22,20 @@ inline int decode_parts(int max_blocks_per_seq, int block_size, int part_tokens)
 }
 
 // Launch plan of the matrix-core decode: `rows` = sequences x head groups.
-// With at least one row per compute unit and contexts up to 2048 tokens, one
-// 8-wave workgroup takes a whole context (no split, no reduce); otherwise the
-// context is split into 512-token partitions for 4-wave workgroups and the
-// partial results are merged by the reduce kernel.
+// - With at least one row per compute unit and contexts up to 2048 tokens,
+//   one 8-wave workgroup takes a whole context (no split, no reduce).
+// - Otherwise the context is split into partitions merged by the reduce
+//   kernel: the longest of 4096, 2048 or 1024 tokens that still gives at
+//   least kDecodeWgsPerCU workgroups per compute unit, for 8-wave workgroups
+//   (fewer, longer partitions: fewer workgroup start-ups and a smaller
+//   reduce); when even 1024-token partitions leave the chip short of work,
+//   512-token partitions for 4-wave workgroups.
 struct DecodePlan {
   int waves;
   int part_tokens;
 };
+constexpr int kDecodeMaxPart = 4096;
+constexpr int kDecodeWgsPerCU = 4;
 inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size) {
   const long long rows = (long long)num_seqs * groups;
   const long long max_ctx = (long long)max_blocks_per_seq * block_size;
@@ -37,6 +43,9 @@ inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, 
     const int part = (int)((max_ctx + kDecodePart - 1) / kDecodePart * kDecodePart);
     return {8, part};
   }
+  for (int part = kDecodeMaxPart; part >= 2 * kDecodePart; part /= 2)
+    if (rows * ((max_ctx + part - 1) / part) >= (long long)kDecodeWgsPerCU * kNumCUs)
+      return {8, part};
   return {4, kDecodePart};
 }
 

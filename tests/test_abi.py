@@ -111,8 +111,11 @@ def test_decode_workspace_size(L):
 
 def test_decode_partition_plan(L):
     f = L.pkv_decode_partition_tokens
-    # long contexts: 512-token partitions
-    assert f(4, 64, 8, 1024, 128, 2) == 512
+    # long contexts: the longest partition (up to 4096 tokens) that still
+    # gives 4 workgroups per compute unit
+    assert f(4, 64, 8, 1024, 128, 2) == 4096
+    assert f(1, 64, 8, 1024, 128, 2) == 1024
+    assert f(16, 32, 32, 256, 16, 1) == 2048
     # a batch with one (sequence, head group) row per compute unit and 2048-token
     # contexts takes whole contexts per workgroup
     assert f(8, 32, 32, 128, 16, 1) == 2048

@@ -103,8 +103,8 @@ def test_ragged_gqa_decode_full_size():
 
 
 def test_long_context_decode_sampled():
-    """Batch 4 x 131072, 64/8 heads: 256 partitions per sequence, then the
-    reduce. The oracle checks a sample of (sequence, head) pairs that covers
+    """Batch 4 x 131072, 64/8 heads: 32 partitions of 4096 tokens per
+    (sequence, kv head), then the reduce. The oracle checks a sample of (sequence, head) pairs that covers
     every sequence and every kv head."""
     case = wl.workload(5)
     rng = np.random.default_rng(0)
@@ -128,3 +128,70 @@ def test_decode_group_larger_than_one_tile():
     """64 query heads per kv head: four 16-head workgroups share a kv head."""
     case = wl.decode_case(910, [700, 33, 1600], 64, 1, 128, 32, "bf16")
     check_decode(case)
+
+
+def _garbage_workspace(case):
+    need = binding.paged_attention_decode_workspace_size(
+        case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq, case.block_size)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws.fill_(0x7F)   # stale contents: NaN-like floats, huge piece counts
+    return ws
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_decode_ragged_block_sizes_stale_workspace(bs):
+    """Ragged batch of 40 sequences x 8 kv heads with empty rows (whole
+    contexts per workgroup); the workspace starts with stale contents and the
+    output with NaN."""
+    rng = np.random.default_rng(bs)
+    lens = rng.integers(1, 2049, size=40).tolist()
+    lens[3] = lens[17] = 0
+    lens[5], lens[6], lens[7] = 1, 16, 17
+    case = wl.decode_case(1300 + bs, lens, 32, 8, 128, bs, "bf16", spare=0.1)
+    dc = DeviceCase(case)
+    dc.out.fill_(float("nan"))
+    ws = _garbage_workspace(case)
+    binding.paged_attention_decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_table,
+                                   dc.seq_lens, bs, case.scale, workspace=ws)
+    got = to_host(dc.out, "bf16")
+    k, v = oracle_pools(case)
+    want = oracle.decode(case.q, k, v, case.block_table, case.seq_lens, bs, case.scale, "bf16")
+    assert np.all(got[3] == 0) and np.all(got[17] == 0)
+    assert max_abs_err(got, want, "bf16") <= ATOL["bf16"]
+
+
+def test_decode_few_rows_full_partitions():
+    """Two sequences x 2 kv heads of up to 2048 tokens: every partition of
+    the workspace is used."""
+    check_decode(wl.decode_case(1400, [2048, 1999], 8, 2, 128, 16, "f16"))
+
+
+def test_decode_wide_batch_whole_contexts():
+    """300 sequences x 8 kv heads (2400 rows) with contexts up to 1024: whole
+    contexts per workgroup, far more workgroups than compute units."""
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 900, size=300).tolist()
+    lens[0] = 1024
+    case = wl.decode_case(1401, lens, 8, 8, 64, 16, "f16", spare=0.1)
+    check_decode(case)
+
+
+# Launch plans with longer partitions: (context lengths, Hq, Hkv, D, expected
+# partition tokens). Lengths sit on and around partition and block edges;
+# block size 16, so a 4096-token partition stages 256 block ids.
+LONG_PLANS = [
+    ([1, 2047, 2048, 2049, 4095, 4096, 0, 3000] * 2, 32, 32, 64, 2048),
+    ([16384, 16383, 4097, 4096, 8191, 1, 0, 12288], 32, 32, 128, 4096),
+    ([16384, 9000], 32, 32, 128, 1024),
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,part", LONG_PLANS)
+def test_decode_long_partition_plans(lens, hq, hkv, d, part):
+    case = wl.decode_case(1500 + part, lens, hq, hkv, d, 16, "bf16", spare=0.05)
+    assert binding.decode_partition_tokens(len(lens), hq, hkv, case.max_blocks_per_seq, 16,
+                                           torch.bfloat16) == part
+    rng = np.random.default_rng(part)
+    pairs = sorted({(b, int(h)) for b in range(len(lens))
+                    for h in rng.choice(hq, size=4, replace=False)} | {(b, hq - 1) for b in range(len(lens))})
+    check_decode(case, pairs=pairs)

@@ -134,3 +134,14 @@ def test_int8_long_context_sampled():
     rng = np.random.default_rng(1)
     pairs = [(b, int(h)) for b in range(2) for h in rng.choice(64, size=6, replace=False)]
     check_decode(Int8Case(case), pairs=pairs)
+
+
+def test_int8_decode_4096_partitions():
+    """256 rows of up to 16384 tokens (bs 16): 4096-token partitions."""
+    lens = [16384, 5000, 0, 12000, 8192, 4096, 1, 9000]
+    case = wl.decode_case(680, lens, 32, 32, 128, 16, "f16", spare=0.05)
+    assert binding.decode_partition_tokens(len(lens), 32, 32, case.max_blocks_per_seq, 16,
+                                           torch.float16) == 4096
+    rng = np.random.default_rng(3)
+    pairs = sorted({(b, int(h)) for b in range(len(lens)) for h in rng.choice(32, size=4, replace=False)})
+    check_decode(Int8Case(case), pairs=pairs)

@@ -114,3 +114,16 @@ def test_varlen_ex_alibi_only_named_workload():
     case = wl.workload(4)
     rows = [(r, h) for r in range(case.q.shape[0]) for h in (0, 9, 22, 31)]
     check_varlen_ex(case, wl.alibi_slopes(32), 512, rows=rows)
+
+
+@pytest.mark.parametrize("window", [3000, 9000])
+def test_decode_ex_4096_partitions_window(window):
+    """256 rows of up to 16384 tokens: 4096-token partitions; those below
+    the window exit and the reduce starts at the first visible one."""
+    lens = [16384, 16383, 4097, 4096, 8191, 1, 0, 12288]
+    case = wl.decode_case(840, lens, 32, 32, 128, 16, "f16", spare=0.05)
+    assert binding.decode_partition_tokens(len(lens), 32, 32, case.max_blocks_per_seq, 16,
+                                           torch.float16) == 4096
+    rng = np.random.default_rng(window)
+    pairs = sorted({(b, int(h)) for b in range(len(lens)) for h in rng.choice(32, size=4, replace=False)})
+    check_decode_ex(case, wl.alibi_slopes(32), window, pairs=pairs)
