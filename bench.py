@@ -8,8 +8,9 @@ One step = one pass of the decode hot path over the LLaMA-7B-shaped batch
 (8 sequences x 2048 tokens, 32/32 heads, head_dim 128, block_size 16, pool
 4096 blocks, fp16): the new token of every sequence is scattered into the
 pool through slot_mapping (paged_kv_write), then every sequence's query
-attends over its 2048 paged tokens (paged_attention_decode: split-KV
-partition pass + log-sum-exp reduce). Inputs are synthetic (N(0,1) values,
+attends over its 2048 paged tokens (paged_attention_decode; on this batch
+one workgroup per whole context, no split and no reduce). Inputs are
+synthetic (N(0,1) values,
 a seeded random block permutation) and resident in HBM before timing. A
 1 GiB buffer is read between timed steps so that the 256 MB Infinity Cache
 does not serve the KV reads (a read, so that no dirty lines are left behind).
@@ -81,6 +82,49 @@ class Timer:
         self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
 
 
+class KernelEvents:
+    """hipEvent_t pairs (timing enabled) that the library's measurement hook
+    (pkv_time_next_kernel) has one kernel launch record at its own dispatch
+    start and end: the kernel's execution time, as a kernel trace reports
+    it, without the event-packet gaps that events around a call include.
+    The events come from the HIP runtime this process already loaded."""
+
+    def __init__(self, n):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a.value, b.value))
+
+    def arm(self, binding, i):
+        binding.time_next_kernel(*self.pairs[i])
+
+    def ms(self, i):
+        out = self.ct.c_float()
+        a, b = self.pairs[i]
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a),
+                                        self.ct.c_void_p(b)):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(self.ct.c_void_p(a))
+            self.hip.hipEventDestroy(self.ct.c_void_p(b))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -146,6 +190,19 @@ def main():
         binding.paged_kv_write(t["k"], t["v"], new_key, new_val, new_slots)
         run_decode(meta, t)
 
+    def kernel_pass(fn, n):
+        """ms of the first kernel of each of n calls, from events the kernel
+        dispatch records (pkv_time_next_kernel)."""
+        ke = KernelEvents(n)
+        for i in range(n):
+            evict()
+            ke.arm(binding, i)
+            fn()
+        torch.cuda.synchronize()
+        kms = [ke.ms(i) for i in range(n)]
+        ke.close()
+        return kms
+
     for _ in range(args.warmup):
         evict()
         step()
@@ -165,6 +222,12 @@ def main():
     step_ms = [a.elapsed_time(c) for a, b, c in tm.ev]
     dec_ms = [b.elapsed_time(c) for a, b, c in tm.ev]
     write_ms = [a.elapsed_time(b) for a, b, c in tm.ev]
+    # kernel-level pass right after the timed steps, same inputs and cache
+    # flush: the decode kernel records dispatch events (arming them makes the
+    # runtime add gaps around the call, so the timed steps run unarmed)
+    kern_ms = kernel_pass(lambda: run_decode(meta, t), args.steps)
+    kern_mean = statistics.mean(kern_ms)
+    kern_gbs = meta.decode_bytes() / (kern_mean * 1e-3) / 1e9
     ms_per_step = statistics.mean(step_ms)
     e = wl.ELEM_BYTES[meta.dtype]
     write_bytes = 2 * 2 * meta.num_seqs * meta.num_kv_heads * meta.head_dim * e + 4 * meta.num_seqs
@@ -201,6 +264,9 @@ def main():
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_call_us": round(dec_mean * 1e3, 2),
         "decode_call_gbs": round(dec_gbs, 1),
+        "decode_kernel_us": round(kern_mean * 1e3, 2),
+        "decode_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                                     round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
         "kv_write_call_us": round(statistics.mean(write_ms) * 1e3, 2),
         "step_bytes": step_bytes,
         "timed_wall_s": round(wall, 4),
@@ -209,11 +275,14 @@ def main():
     result["roofline"] = {
         "kernel": "decode_mfma_kernel (one launch per paged_attention_decode call on this batch: "
                   "8-wave workgroups, one whole 2048-token context each, no split)",
-        "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
         "algorithmic_bytes_per_launch": meta.decode_bytes(),
-        "timing": "HIP events around each call on the launch stream (includes ~3-4 us of "
-                  "event/launch overhead; the kernel trace gives the kernel alone)",
+        "timing": "per launch: HIP events recorded by the kernel dispatch itself "
+                  "(hipExtLaunchKernel through pkv_time_next_kernel) on the launch stream, "
+                  "mean over a pass of as many calls as timed steps that follows them "
+                  "(same inputs, same cache flush); events around the whole call "
+                  "(decode_call_us) add the event-packet gaps",
     }
     if trec is not None:
         result["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)
@@ -224,6 +293,8 @@ def main():
     # other paths of the hot loop (same method: events per call, cache flush)
     # ------------------------------------------------------------------
     def time_calls(fn, n, warm=3):
+        """Per call: ms between events around the call; then, in a pass of
+        its own, ms of the call's first kernel from dispatch-recorded events."""
         for _ in range(warm):
             evict()
             fn()
@@ -236,7 +307,7 @@ def main():
             fn()
             b.record()
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in evs]
+        return [a.elapsed_time(b) for a, b in evs], kernel_pass(fn, n)
 
     if not args.no_extra:
         n_extra = max(5, min(args.steps, 20))
@@ -244,12 +315,16 @@ def main():
         for c in (3, 5):
             m = wl.workload(c, values=False)
             tt = decode_setup(m)
-            ms = time_calls(lambda: run_decode(m, tt), n_extra)
+            ms, kms = time_calls(lambda: run_decode(m, tt), n_extra)
             mu = statistics.mean(ms)
             gbs = m.decode_bytes() / (mu * 1e-3) / 1e9
             extra[m.name] = {"us": round(mu * 1e3, 2), "gbs": round(gbs, 1),
                              "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-                             "bytes": m.decode_bytes()}
+                             "bytes": m.decode_bytes(),
+                             "kernel_us": round(statistics.mean(kms) * 1e3, 2),
+                             "partition_tokens": binding.decode_partition_tokens(
+                                 m.num_seqs, m.num_q_heads, m.num_kv_heads,
+                                 m.max_blocks_per_seq, m.block_size, tdt(m.dtype))}
             del tt
             torch.cuda.empty_cache()
         # int8 cache on the LLaMA-7B shape: the same decode over 1-byte codes
@@ -265,14 +340,15 @@ def main():
         ws8 = torch.empty(max(1, binding.paged_attention_decode_workspace_size(
             m.num_seqs, m.num_q_heads, m.head_dim, m.max_blocks_per_seq, m.block_size)),
             dtype=torch.uint8, device=dev)
-        ms = time_calls(lambda: binding.paged_attention_decode_int8(
+        ms, kms = time_calls(lambda: binding.paged_attention_decode_int8(
             o8, q8, k8, v8, ksd, vsd, bt8, ctx8, m.block_size, m.scale, workspace=ws8), n_extra)
         mu = statistics.mean(ms)
         b8 = m.decode_bytes() - m.kv_bytes_read() // 2
         gbs = b8 / (mu * 1e-3) / 1e9
         extra["int8_kv_decode_llama7b_b8_ctx2048"] = {
             "us": round(mu * 1e3, 2), "gbs": round(gbs, 1),
-            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b8}
+            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b8,
+            "kernel_us": round(statistics.mean(kms) * 1e3, 2)}
         del k8, v8
         torch.cuda.empty_cache()
         for c in (4, 6):
@@ -286,14 +362,16 @@ def main():
                             device=dev)
             out = torch.empty_like(q)
             cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
-            ms = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
+            ms, kms = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
                             n_extra)
             mu = statistics.mean(ms)
             fl = m.prefill_flops()
             extra[m.name] = {"us": round(mu * 1e3, 2),
                              "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
                              "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                             "flops": fl, "total_q": int(m.cu_seqlens_q[-1])}
+                             "flops": fl, "total_q": int(m.cu_seqlens_q[-1]),
+                             "kernel_us": round(statistics.mean(kms) * 1e3, 2),
+                             "kernel_tflops": round(fl / (statistics.mean(kms) * 1e-3) / 1e12, 2)}
             if c == 6:
                 extra[m.name]["kv_gbs"] = round(m.kv_bytes_read() / (mu * 1e-3) / 1e9, 1)
                 extra[m.name]["kv_bytes"] = m.kv_bytes_read()
@@ -308,7 +386,7 @@ def main():
         tt = decode_setup(m)
         slopes = torch.from_numpy(wl.alibi_slopes(m.num_q_heads)).to(dev)
         win = 1024
-        ms = time_calls(lambda: binding.paged_attention_decode_ex(
+        ms, kms = time_calls(lambda: binding.paged_attention_decode_ex(
             tt["out"], tt["q"], tt["k"], tt["v"], tt["bt"], tt["ctx"], m.block_size, m.scale,
             slopes, win, workspace=tt["ws"]), n_extra)
         mu = statistics.mean(ms)
@@ -317,7 +395,8 @@ def main():
         bw = vis * 2 * m.num_kv_heads * m.head_dim * eb + 2 * m.num_seqs * m.num_q_heads * m.head_dim * eb
         extra["decode_alibi_window1024_llama7b"] = {
             "us": round(mu * 1e3, 2), "gbs": round(bw / (mu * 1e-3) / 1e9, 1),
-            "hbm_peak_frac": round(bw / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": bw}
+            "hbm_peak_frac": round(bw / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": bw,
+            "kernel_us": round(statistics.mean(kms) * 1e3, 2)}
         del tt
         torch.cuda.empty_cache()
         m = wl.workload(4, values=False)
@@ -329,7 +408,7 @@ def main():
         cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
         slopes = torch.from_numpy(wl.alibi_slopes(m.num_q_heads)).to(dev)
         win = 512
-        ms = time_calls(lambda: binding.paged_attention_varlen_ex(
+        ms, kms = time_calls(lambda: binding.paged_attention_varlen_ex(
             out, q, cu, k, v, bt, sl, True, slopes, win), n_extra)
         mu = statistics.mean(ms)
         pairs = 0
@@ -339,7 +418,8 @@ def main():
         fl = 4 * m.head_dim * m.num_q_heads * pairs
         extra["prefill_alibi_window512_16seq"] = {
             "us": round(mu * 1e3, 2), "tflops": round(fl / (mu * 1e-3) / 1e12, 2),
-            "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops": fl}
+            "bf16_peak_frac": round(fl / (mu * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops": fl,
+            "kernel_us": round(statistics.mean(kms) * 1e3, 2)}
         del k, v, q, out
         torch.cuda.empty_cache()
         # block manager: host cost of one decode step's scheduling (256
@@ -367,7 +447,7 @@ def main():
         npairs = 1024
         perm = torch.randperm(m.num_blocks)
         pairs = torch.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).to(torch.int32).to(dev)
-        ms = time_calls(lambda: binding.paged_kv_copy_blocks(kc, vc, pairs), n_extra)
+        ms, kms = time_calls(lambda: binding.paged_kv_copy_blocks(kc, vc, pairs), n_extra)
         mu = statistics.mean(ms)
         cbytes = 2 * 2 * npairs * m.block_size * m.num_kv_heads * m.head_dim * 2 + npairs * 8
         extra["block_manager_decode_step_b256"] = {

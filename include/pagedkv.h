@@ -288,6 +288,21 @@ int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32
                                     int32_t max_blocks_per_seq, int32_t block_size,
                                     int32_t dtype);
 
+/*
+ * pkv_time_next_kernel -- measurement hook. The next kernel that the calling
+ * thread launches through this library (the first kernel of its next call:
+ * the attention kernel itself for a decode call whose contexts are split, not
+ * the reduce) records start_event when its dispatch begins and stop_event
+ * when it ends, on the stream it is launched on (hipExtLaunchKernel events),
+ * so that hipEventElapsedTime(start, stop) is that kernel's execution time
+ * without the gaps around it. The events are hipEvent_t handles created by
+ * the caller with timing enabled; either may be NULL. The setting is
+ * per-thread and is consumed by one launch; NULL, NULL cancels it. A call
+ * that fails validation launches nothing and leaves it pending. Returns
+ * PKV_OK.
+ */
+int pkv_time_next_kernel(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pkv_decode_partition_tokens.restype = i32
+        L.pkv_time_next_kernel.argtypes = [vp, vp]
+        L.pkv_time_next_kernel.restype = ctypes.c_int
         L.paged_kv_write_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64,
                                           i32, vp]
         L.paged_kv_write_int8.restype = ctypes.c_int
@@ -472,6 +474,12 @@ class BlockManager:
         if got < 0:
             raise PagedKVError("pkv_bm_take_copies", int(got), status_string(int(got)))
         return out[:got]
+
+
+def time_next_kernel(start_event, stop_event) -> None:
+    """Have the next kernel this thread launches through the library record
+    the two hipEvent_t handles (ints or None) at its dispatch start and end."""
+    lib().pkv_time_next_kernel(start_event, stop_event)
 
 
 def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,

@@ -9,6 +9,20 @@
 #include "pagedkv.h"
 #include "pkv_launch.h"
 
+namespace pkv {
+KernelTiming& pending_timing() {
+  thread_local KernelTiming t;
+  return t;
+}
+}  // namespace pkv
+
+int pkv_time_next_kernel(void* start_event, void* stop_event) {
+  pkv::KernelTiming& t = pkv::pending_timing();
+  t.start = static_cast<hipEvent_t>(start_event);
+  t.stop = static_cast<hipEvent_t>(stop_event);
+  return PKV_OK;
+}
+
 namespace {
 
 bool valid_dtype(int32_t d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }

@@ -568,7 +568,7 @@ template <class Ty, int D>
 static hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream, int log2_bs,
                                 int num_parts, int part_tokens) {
   using S = typename Ty::storage;
-  hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(a.num_q_heads, a.num_seqs),
+  launch_kernel((decode_reduce_kernel<Ty, D>), dim3(a.num_q_heads, a.num_seqs),
                      dim3(kDecThreads), 0, stream, static_cast<S*>(a.out), a.ws_ml, a.ws_o,
                      a.context_lens, a.num_q_heads, log2_bs, a.max_blocks_per_seq, num_parts,
                      part_tokens, a.window_left);
@@ -583,7 +583,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, kDecodePart);
   dim3 grid(parts, a.num_q_heads / G, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<Ty, D, G>), grid, dim3(kDecThreads), 0, stream,
+  launch_kernel((decode_partition_kernel<Ty, D, G>), grid, dim3(kDecThreads), 0, stream,
                      static_cast<S*>(a.out), static_cast<const S*>(a.q),
                      static_cast<const S*>(a.k_cache), static_cast<const S*>(a.v_cache),
                      a.block_table, a.context_lens, a.ws_ml, a.ws_o, scale_log2, a.num_q_heads,
@@ -601,7 +601,7 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
+  launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
                      stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
                      scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw, log2_bs,

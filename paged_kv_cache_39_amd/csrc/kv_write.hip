@@ -40,7 +40,7 @@ hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const 
   const int64_t num_pieces = num_tokens * pieces_per_row;
   const int threads = 256;
   const int64_t blocks = (num_pieces + threads - 1) / threads;
-  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+  launch_kernel(kv_write_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
                      static_cast<const uint4*>(key), static_cast<const uint4*>(value),
                      slot_mapping, num_pieces, pieces_per_row, num_slots);
@@ -77,7 +77,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                               hipStream_t stream) {
   const int64_t num_pieces = num_pairs * pieces_per_block;
   const int threads = 256;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((num_pieces + threads - 1) / threads)),
+  launch_kernel(copy_blocks_kernel, dim3((unsigned)((num_pieces + threads - 1) / threads)),
                      dim3(threads), 0, stream, static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), pairs, num_pieces, pieces_per_block,
                      num_blocks);
@@ -142,17 +142,17 @@ hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, c
   uint4* kc = static_cast<uint4*>(k_cache);
   uint4* vc = static_cast<uint4*>(v_cache);
   if (dtype == 0) {
-    hipLaunchKernelGGL(kv_write_int8_kernel<F32>, grid, dim3(threads), 0, stream, kc, vc,
+    launch_kernel(kv_write_int8_kernel<F32>, grid, dim3(threads), 0, stream, kc, vc,
                        static_cast<const float*>(key), static_cast<const float*>(value), k_scale,
                        v_scale, slot_mapping, num_pieces, pieces_per_row, pieces_per_head,
                        num_slots);
   } else if (dtype == 1) {
-    hipLaunchKernelGGL(kv_write_int8_kernel<F16>, grid, dim3(threads), 0, stream, kc, vc,
+    launch_kernel(kv_write_int8_kernel<F16>, grid, dim3(threads), 0, stream, kc, vc,
                        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                        k_scale, v_scale, slot_mapping, num_pieces, pieces_per_row,
                        pieces_per_head, num_slots);
   } else {
-    hipLaunchKernelGGL(kv_write_int8_kernel<BF16>, grid, dim3(threads), 0, stream, kc, vc,
+    launch_kernel(kv_write_int8_kernel<BF16>, grid, dim3(threads), 0, stream, kc, vc,
                        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                        k_scale, v_scale, slot_mapping, num_pieces, pieces_per_row,
                        pieces_per_head, num_slots);

@@ -2,12 +2,35 @@
 // C-ABI entry points before any of these is called.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pkv_common.h"
 
 namespace pkv {
+
+// Events the calling thread's next kernel launch records at its own dispatch
+// start and end (set by pkv_time_next_kernel; consumed by one launch).
+struct KernelTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+KernelTiming& pending_timing();
+
+// Every kernel of the library is launched through here.
+template <typename... Formals, typename... Actuals>
+inline void launch_kernel(void (*kernel)(Formals...), dim3 grid, dim3 block, uint32_t shmem,
+                          hipStream_t stream, Actuals... args) {
+  KernelTiming& t = pending_timing();
+  if (t.start != nullptr || t.stop != nullptr) {
+    const KernelTiming use = t;
+    t = KernelTiming{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, use.start, use.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+  }
+}
 
 // Tokens per split-KV partition of the decode path (the long-context split),
 // and the longest single partition a decode workgroup takes when the batch

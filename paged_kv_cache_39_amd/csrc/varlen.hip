@@ -535,7 +535,7 @@ static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.total_q + bq - 1) / bq + a.num_seqs;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)a.head_dim);
   dim3 grid((unsigned)(tiles * a.num_kv_heads));
-  hipLaunchKernelGGL((varlen_prefill_kernel<Ty, D, EXT>), grid, dim3(kVlThreads), 0, stream,
+  launch_kernel((varlen_prefill_kernel<Ty, D, EXT>), grid, dim3(kVlThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
                      static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens,

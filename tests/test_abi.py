@@ -210,3 +210,8 @@ def test_copy_blocks_validation(L):
 def test_block_manager_exports(L):
     for name in ("pkv_bm_create", "pkv_bm_append", "pkv_bm_take_copies", "pkv_bm_block_table"):
         assert name in declared_functions() and hasattr(L, name)
+
+
+def test_time_next_kernel_without_events(L):
+    # NULL, NULL cancels the hook; no HIP call is made
+    assert L.pkv_time_next_kernel(None, None) == 0
