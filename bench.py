@@ -41,7 +41,7 @@ FLUSH_BYTES = 1 << 30          # read between timed steps (4x the Infinity Cache
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the decode step workload")
@@ -265,6 +265,7 @@ def main():
         "decode_call_us": round(dec_mean * 1e3, 2),
         "decode_call_gbs": round(dec_gbs, 1),
         "decode_kernel_us": round(kern_mean * 1e3, 2),
+        "decode_kernel_us_median": round(statistics.median(kern_ms) * 1e3, 2),
         "decode_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                                      round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
         "kv_write_call_us": round(statistics.mean(write_ms) * 1e3, 2),
