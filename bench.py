@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the decode step workload")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the packed causal prefill workload (for counter runs)")
     return ap.parse_args()
 
 
@@ -157,6 +159,33 @@ def main():
 
     def ints(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    if args.prefill_only:
+        # the packed causal prefill alone: W warm-up calls, then K timed calls
+        m = wl.workload(4, values=False)
+        dtp = tdt(m.dtype)
+        k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
+        v = torch.randn_like(k)
+        q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp, device=dev)
+        out = torch.empty_like(q)
+        cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
+        for _ in range(args.warmup):
+            evict()
+            binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            evict()
+            a.record()
+            binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True)
+            b.record()
+        torch.cuda.synchronize()
+        mu = statistics.mean([a.elapsed_time(b) for a, b in evs])
+        fl = m.prefill_flops()
+        print(json.dumps({"workload": m.name, "steps": args.steps, "us": round(mu * 1e3, 2),
+                          "tflops": round(fl / (mu * 1e-3) / 1e12, 2), "flops": fl}))
+        return
 
     def decode_setup(meta):
         dt = tdt(meta.dtype)
