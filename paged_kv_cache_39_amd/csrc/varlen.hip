@@ -29,7 +29,6 @@ constexpr int kVlThreads = kVlWaves * kWave;
 constexpr int kVlRows = 128;      // rows per workgroup = query positions x heads of the group
 constexpr int kVlRowsWave = 32;   // two 16-row MFMA tiles per wave
 constexpr int kVlBN = 64;         // keys per KV tile
-constexpr int kNumXcds = 8;       // accelerator complex dies of an MI355X
 
 // K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
 // 16-byte slots: slot s of row r holds chunk s ^ f(r). The functions were
@@ -127,6 +126,101 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
   return false;
 }
 
+// Key tiles (of kVlBN keys) that a query tile's loop runs over: up to its
+// rows' highest visible key, i + Lk - Lq for the tile's last row i under the
+// causal mask, else Lk. That bound grows with the tile's position, so the
+// tiles of a sequence needing at least w key tiles form a suffix; this
+// returns its length (lq, lk: the sequence's query and key counts).
+__device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, int causal) {
+  if (lq <= 0) return 0;
+  const int nt = (lq + bq - 1) / bq;
+  if (w <= 0) return nt;
+  const int kmin = (w - 1) * kVlBN;   // the loop end must exceed this
+  if (lk <= kmin) return 0;
+  if (!causal) return nt;
+  const int x = kmin - (lk - lq);      // needs min((t + 1) * bq, lq) > x
+  if (lq <= x) return 0;
+  return x < 0 ? nt : nt - x / bq;
+}
+
+// Locate query tile `g` of one kv head in longest-first order: tiles sorted
+// by their key-tile count, most first (ties by sequence, then position), so
+// the longest loops start first and the shortest fill the tail. A binary
+// search over the count finds g's bucket; a scan over the sequences finds
+// the tile in it. One wave runs this; returns false when g is past the last
+// tile. (my_lq, my_lk): sequence `lane`'s counts (the first 64 sequences;
+// further ones are read from memory).
+__device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ seq_lens,
+                                              int num_seqs, int total_q, int max_lk, int bq,
+                                              int causal, int g, int lane, int my_lq, int my_lk,
+                                              int& seq, int& q0) {
+  auto meta = [&](int s0, int& lq, int& lk) {
+    if (s0 == 0) {
+      lq = my_lq;
+      lk = my_lk;
+      return;
+    }
+    const int s = s0 + lane;
+    lq = 0;
+    lk = 0;
+    if (s < num_seqs) {
+      const int r0 = max(0, min(cu[s], total_q));
+      lq = max(0, min(cu[s + 1], total_q) - r0);
+      lk = max(0, min(seq_lens[s], max_lk));
+    }
+  };
+  auto count = [&](int w) {   // tiles needing at least w key tiles
+    int c = 0;
+    for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
+      int lq, lk;
+      meta(s0, lq, lk);
+      c += tiles_with_work(w, lq, lk, bq, causal);
+    }
+    return wave_sum(c);
+  };
+  if (g >= count(0)) return false;
+  int wmax = 0;
+  for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
+    int lq, lk;
+    meta(s0, lq, lk);
+    wmax = max(wmax, (lk + kVlBN - 1) / kVlBN);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
+  int lo = 0, hi = wmax + 1;   // count(lo) > g >= count(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count(mid) > g) lo = mid;
+    else hi = mid;
+  }
+  int r = g - count(lo + 1);   // rank among the tiles needing exactly lo key tiles
+  for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
+    int lq, lk;
+    meta(s0, lq, lk);
+    const int ge = tiles_with_work(lo, lq, lk, bq, causal);
+    const int c = ge - tiles_with_work(lo + 1, lq, lk, bq, causal);
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (r < total) {
+      const unsigned long long hit = __ballot(incl - c <= r && r < incl);
+      const int L = __builtin_ctzll(hit);
+      const int nt = (__shfl(lq, L, kWave) + bq - 1) / bq;
+      const int t = nt - __shfl(ge, L, kWave) + (r - __shfl(incl - c, L, kWave));
+      seq = s0 + L;
+      q0 = t * bq;
+      return true;
+    }
+    r -= total;
+  }
+  return false;
+}
+
 // EXT: the attention variants -- a sliding window (keys j >= p - window_left
 // for the query at p = i + Lk - Lq, window_left >= 0) and ALiBi (score +
 // alibi[h] * (j - p)); alibi may be NULL and window_left negative.
@@ -137,7 +231,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2,
-    int tiles_per_head, const float* __restrict__ alibi, int window_left) {
+    const float* __restrict__ alibi, int window_left) {
   using L = VlLds<D>;
   constexpr int KS = D / 32;                 // k-steps of the QK product
   constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
@@ -152,16 +246,13 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps derived addresses scalar
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-  // L2). Renumber them so that every XCD takes a contiguous range of
-  // (kv head, query tile): the tiles that stream one kv head's K/V then
-  // share an L2.
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x % kNumXcds, k_in = blockIdx.x / kNumXcds;
-  const int per = nwg / kNumXcds, rem = nwg % kNumXcds;
-  const int logical = xcd * per + min(xcd, rem) + k_in;
-  const int kvh = logical / tiles_per_head;
-  const int tile = logical - kvh * tiles_per_head;
+  // Workgroups are dispatched in index order, round-robin over the 8 XCDs
+  // (each with its own L2). Index = tile rank x Hkv + kv head: every kv
+  // head's heaviest tiles start first, and when Hkv is a multiple of 8 each
+  // XCD serves fixed kv heads, whose K/V then stay in its L2 (with fewer kv
+  // heads, a head's tiles alternate over the XCDs).
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int tile = blockIdx.x / num_kv_heads;
   const int group = num_q_heads / num_kv_heads;
   const int bq = kVlRows / group;   // query positions per tile
   const int bs = 1 << log2_bs;
@@ -178,7 +269,15 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
     const int nt0 = my_lq > 0 ? (my_lq + bq - 1) / bq : 0;
     int seq = -1, q0 = 0, r0 = 0, lq_ = 0, lk_ = 0;
-    if (!find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)) seq = -1;
+    // longest-first order; under a window a tile's key count is not
+    // monotone in its position, so those tiles go by rank from the end
+    const bool found =
+        (EXT && window_left >= 0)
+            ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
+            : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
+                            max_blocks_per_seq << log2_bs, bq, causal, tile, lane, my_lq, my_lk,
+                            seq, q0);
+    if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
       r0 = __shfl(my_r0, seq, kWave);
       lq_ = __shfl(my_lq, seq, kWave);
@@ -541,7 +640,7 @@ static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
                      static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens,
                      a.causal, a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
                      __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks,
-                     scale_log2, (int)tiles, a.alibi, a.window_left);
+                     scale_log2, a.alibi, a.window_left);
   return hipGetLastError();
 }
 
