@@ -456,6 +456,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int vbyte = 8 * (l16 & 1);
   const int vchunk = (l16 & 3) >> 1;
 
+  // A wave whose rows are all padding (a tile of a few queries, such as the
+  // decode rows of a mixed batch) only helps stage the tiles and skips the
+  // arithmetic.
+  const bool wave_live = __builtin_amdgcn_ballot_w64(row_ok[0] || row_ok[1]) != 0;
+
   int it = 0;
   for (int kv0 = kv_begin; kv0 < kv_end; kv0 += kVlBN, ++it) {
     const int cur = it & 1;
@@ -469,142 +474,143 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const uint8_t* sk = s_kv + cur * L::stageB;
     const uint8_t* sv = sk + L::tileB;
     const bool need_mask = kv0 + kVlBN > nomask_end || (windowed && kv0 < mask_lo_end);
-
-    // Operand reads from LDS are issued a phase ahead of the MFMAs that use
-    // them, so their latency hides behind the softmax arithmetic:
-    //   K operands of half h+1 and V^T operands of half h are read, the
-    //   softmax of half h runs, then q.k of half h+1 and p.v of half h issue.
-    auto read_k = [&](int hh, u32x4_t (&ka)[2][KS]) {
+    if (wave_live) {
+      // Operand reads from LDS are issued a phase ahead of the MFMAs that use
+      // them, so their latency hides behind the softmax arithmetic:
+      //   K operands of half h+1 and V^T operands of half h are read, the
+      //   softmax of half h runs, then q.k of half h+1 and p.v of half h issue.
+      auto read_k = [&](int hh, u32x4_t (&ka)[2][KS]) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int r = 32 * hh + 16 * n + l16;
+        for (int n = 0; n < 2; ++n) {
+          const int r = 32 * hh + 16 * n + l16;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot_k(r, 4 * s + g4) * 16);
-      }
-    };
-    auto qk = [&](const u32x4_t (&ka)[2][KS], f32x4_t (&st)[2][2]) {
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          st[n][0] = Mma<Ty>::mfma(ka[n][s], qb[0][s], st[n][0]);
-          st[n][1] = Mma<Ty>::mfma(ka[n][s], qb[1][s], st[n][1]);
+          for (int s = 0; s < KS; ++s)
+            ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot_k(r, 4 * s + g4) * 16);
         }
-      }
-    };
-    auto read_v = [&](int hh, u32x4_t (&va)[ND]) {
-      const int r0 = 32 * hh + vrow, r1 = r0 + 16;
+      };
+      auto qk = [&](const u32x4_t (&ka)[2][KS], f32x4_t (&st)[2][2]) {
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const int c = 2 * nd + vchunk;
-        const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot_v(r0, c) * 16 + vbyte);
-        const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot_v(r1, c) * 16 + vbyte);
-        va[nd] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
-    };
+        for (int n = 0; n < 2; ++n) {
+          st[n][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          st[n][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            st[n][0] = Mma<Ty>::mfma(ka[n][s], qb[0][s], st[n][0]);
+            st[n][1] = Mma<Ty>::mfma(ka[n][s], qb[1][s], st[n][1]);
+          }
+        }
+      };
+      auto read_v = [&](int hh, u32x4_t (&va)[ND]) {
+        const int r0 = 32 * hh + vrow, r1 = r0 + 16;
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          const int c = 2 * nd + vchunk;
+          const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot_v(r0, c) * 16 + vbyte);
+          const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot_v(r1, c) * 16 + vbyte);
+          va[nd] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      };
 
-    f32x4_t st_cur[2][2];
-    {
-      u32x4_t ka[2][KS];
-      read_k(0, ka);
-      qk(ka, st_cur);
-    }
+      f32x4_t st_cur[2][2];
+      {
+        u32x4_t ka[2][KS];
+        read_k(0, ka);
+        qk(ka, st_cur);
+      }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
-      u32x4_t ka[2][KS];
-      u32x4_t va[ND];
-      if (hh == 0) read_k(1, ka);
-      read_v(hh, va);
-      // ---- online softmax; lane's keys: kv0 + 32hh + 16n + 4*g4 + i ----
-      // Scores stay unscaled: the max is taken on raw q.k (the scale is
-      // positive) and the exponent is one fma, s*scale - m.
-      if (need_mask) {
-        // key kv0 + 32hh + 16n + 4*g4 + i is visible iff 32hh + 16n + i <= thr
-        // (and, with a window, >= thr_lo)
+      for (int hh = 0; hh < 2; ++hh) {   // two halves of 32 keys
+        u32x4_t ka[2][KS];
+        u32x4_t va[ND];
+        if (hh == 0) read_k(1, ka);
+        read_v(hh, va);
+        // ---- online softmax; lane's keys: kv0 + 32hh + 16n + 4*g4 + i ----
+        // Scores stay unscaled: the max is taken on raw q.k (the scale is
+        // positive) and the exponent is one fma, s*scale - m.
+        if (need_mask) {
+          // key kv0 + 32hh + 16n + 4*g4 + i is visible iff 32hh + 16n + i <= thr
+          // (and, with a window, >= thr_lo)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const int thr = lim[mt] - kv0 - 4 * g4;
+            const int thr_lo = wlo[mt] - kv0 - 4 * g4;
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int o = 32 * hh + 16 * n + i;
+                const bool vis = EXT ? (o <= thr && o >= thr_lo) : (o <= thr);
+                st_cur[n][mt][i] = vis ? st_cur[n][mt][i] : -INFINITY;
+              }
+          }
+        }
+        // variants: scores are scaled and biased here (the max must see the
+        // bias), so the exponent below takes a unit scale
+        if constexpr (EXT) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const float dj0 = (float)(kv0 + 32 * hh + 4 * g4 - p_abs[mt]);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                st_cur[n][mt][i] =
+                    fmaf(st_cur[n][mt][i], scale_log2, al2[mt] * (dj0 + (float)(16 * n + i)));
+          }
+        }
+        constexpr float one = 1.f;
+        const float sc = EXT ? one : scale_log2;
+        // lane-local maxima (raw scores); the row max over the 4 lane groups is
+        // only needed when the running max has to move
+        // (maximum, not fmax: no NaN canonicalisation of the MFMA results)
+        float mx[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int thr = lim[mt] - kv0 - 4 * g4;
-          const int thr_lo = wlo[mt] - kv0 - 4 * g4;
+          float a = st_cur[0][mt][0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) a = __builtin_elementwise_maximum(a, st_cur[k >> 2][mt][k & 3]);
+          mx[mt] = a * sc;
+        }
+        const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            float m = mx[mt];
+            m = fmaxf(m, shfl_xor_f(m, 16));
+            m = fmaxf(m, shfl_xor_f(m, 32));
+            const float mnew = fmaxf(m_use[mt], m);
+            const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
+            m_use[mt] = mnew;
+            nref[mt] = -safe_max_ref(mnew);
+            lacc[mt] *= alpha;
+#pragma unroll
+            for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
+          }
+        }
+        u32x4_t pb[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          float pv[2][4];
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int o = 32 * hh + 16 * n + i;
-              const bool vis = EXT ? (o <= thr && o >= thr_lo) : (o <= thr);
-              st_cur[n][mt][i] = vis ? st_cur[n][mt][i] : -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], sc, nref[mt]));
+          pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
+          pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
+          pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
+          pb[mt][3] = Mma<Ty>::pack(pv[1][2], pv[1][3]);
         }
-      }
-      // variants: scores are scaled and biased here (the max must see the
-      // bias), so the exponent below takes a unit scale
-      if constexpr (EXT) {
+        // ---- q.k of the next half, then O^T += V^T P^T over these 32 keys ----
+        if (hh == 0) qk(ka, st_cur);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const float dj0 = (float)(kv0 + 32 * hh + 4 * g4 - p_abs[mt]);
-#pragma unroll
-          for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              st_cur[n][mt][i] =
-                  fmaf(st_cur[n][mt][i], scale_log2, al2[mt] * (dj0 + (float)(16 * n + i)));
+          // row sums of the rounded P on the matrix cores: a V^T tile of ones
+          lacc[mt] = Mma<Ty>::mfma(ones, pb[mt], lacc[mt]);
         }
-      }
-      constexpr float one = 1.f;
-      const float sc = EXT ? one : scale_log2;
-      // lane-local maxima (raw scores); the row max over the 4 lane groups is
-      // only needed when the running max has to move
-      // (maximum, not fmax: no NaN canonicalisation of the MFMA results)
-      float mx[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float a = st_cur[0][mt][0];
-#pragma unroll
-        for (int k = 1; k < 8; ++k) a = __builtin_elementwise_maximum(a, st_cur[k >> 2][mt][k & 3]);
-        mx[mt] = a * sc;
-      }
-      const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          float m = mx[mt];
-          m = fmaxf(m, shfl_xor_f(m, 16));
-          m = fmaxf(m, shfl_xor_f(m, 32));
-          const float mnew = fmaxf(m_use[mt], m);
-          const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
-          m_use[mt] = mnew;
-          nref[mt] = -safe_max_ref(mnew);
-          lacc[mt] *= alpha;
-#pragma unroll
-          for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
+        for (int nd = 0; nd < ND; ++nd) {
+          acc[0][nd] = Mma<Ty>::mfma(va[nd], pb[0], acc[0][nd]);
+          acc[1][nd] = Mma<Ty>::mfma(va[nd], pb[1], acc[1][nd]);
         }
-      }
-      u32x4_t pb[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float pv[2][4];
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[n][i] = fast_exp2(fmaf(st_cur[n][mt][i], sc, nref[mt]));
-        pb[mt][0] = Mma<Ty>::pack(pv[0][0], pv[0][1]);
-        pb[mt][1] = Mma<Ty>::pack(pv[0][2], pv[0][3]);
-        pb[mt][2] = Mma<Ty>::pack(pv[1][0], pv[1][1]);
-        pb[mt][3] = Mma<Ty>::pack(pv[1][2], pv[1][3]);
-      }
-      // ---- q.k of the next half, then O^T += V^T P^T over these 32 keys ----
-      if (hh == 0) qk(ka, st_cur);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // row sums of the rounded P on the matrix cores: a V^T tile of ones
-        lacc[mt] = Mma<Ty>::mfma(ones, pb[mt], lacc[mt]);
-      }
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        acc[0][nd] = Mma<Ty>::mfma(va[nd], pb[0], acc[0][nd]);
-        acc[1][nd] = Mma<Ty>::mfma(va[nd], pb[1], acc[1][nd]);
       }
     }
     barrier_lds_ops();   // every wave is done with this stage before it is refilled

@@ -70,6 +70,21 @@ def test_varlen_many_sequences():
     check_varlen(case)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_many_sequences_ragged_queries(causal):
+    """130 sequences (two wave-wide chunks for the tile lookup) with empty,
+    single-query and chunked rows (Lk > Lq): longest-first tile order over
+    buckets that span both chunks."""
+    rng = np.random.default_rng(11)
+    ql = rng.integers(0, 24, size=130)
+    kl = ql + rng.integers(0, 300, size=130)
+    ql[[0, 64, 65, 129]] = 0
+    ql[[1, 70]] = 1
+    case = wl.varlen_case(710 + causal, ql.tolist(), kl.tolist(), 8, 2, 64, 16, "f16",
+                          causal=causal)
+    check_varlen(case)
+
+
 def test_packed_prefill_named_workload():
     """16 sequences, lengths log-uniform in [64, 2048], 32/8 heads, bs 128:
     every query row of a sample of heads checked, covering every sequence."""
