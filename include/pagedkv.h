@@ -206,6 +206,47 @@ int paged_attention_varlen_ex(void* out, const void* q, const int32_t* cu_seqlen
                               int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
+ * Split varlen: long key ranges over several workgroups
+ * -----------------------------------------------------
+ * paged_attention_varlen_split computes exactly what paged_attention_varlen
+ * computes (same arguments and reading), for batches where a few query rows
+ * sit over long contexts -- the decode rows of a mixed decode + prefill
+ * batch, or the last few queries of a prefill over a long context. The last
+ * query tile of a sequence, when its (query, head) rows fit one wave (at
+ * most 32: e.g. up to 8 queries with 4 query heads per kv head) and its keys
+ * run past one chunk, is cut into chunks attended by separate workgroups,
+ * and their partial softmax results are merged exactly with the log-sum-exp
+ * rule of the split decode (the vLLM-on-CANN page: scattered blocks merged
+ * block by block with an online softmax). Chunks hold at least 512 keys; a
+ * tile is cut into at most 16 of them. Full tiles are not cut (they already
+ * spread over many workgroups).
+ *
+ * paged_attention_varlen_workspace_size -- bytes of device workspace the
+ * split call needs for these sizes: per chunk, fp32 (max, sum) and the
+ * unnormalised output of the (up to 32) rows of each sequence's last tile
+ * per kv head. 0 when no tile can be cut (contexts of at most 512 keys: the
+ * split call then is the plain one) and for invalid sizes.
+ *
+ *   workspace : device scratch of workspace_bytes bytes, workspace_bytes >=
+ *               paged_attention_varlen_workspace_size(...) (may be NULL when
+ *               that is 0). Its contents on entry do not matter; it is
+ *               clobbered. Calls that share a workspace must be ordered on
+ *               one stream.
+ * Returns PKV_ERR_WORKSPACE when it is missing or too small; other statuses
+ * as paged_attention_varlen.
+ */
+size_t paged_attention_varlen_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq,
+                                             int32_t block_size);
+int paged_attention_varlen_split(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, int causal,
+                                 int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Int8 KV cache
  * -------------
  * The skill page lists int8 KV-cache quantisation among the ways to shrink

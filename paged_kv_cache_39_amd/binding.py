@@ -79,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_varlen_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                                 i32, i32, i64, i32, i32, i32, i32, i32, i64, i32,
                                                 vp]
+        L.paged_attention_varlen_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.paged_attention_varlen_workspace_size.restype = sz
+        L.paged_attention_varlen_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32,
+                                                   i64, i32, i32, i32, i32, i32, i64, i32, vp,
+                                                   sz, vp]
         L.paged_attention_varlen_ex.restype = ctypes.c_int
         L.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
         L.paged_kv_copy_blocks.restype = ctypes.c_int
@@ -242,6 +247,46 @@ def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, 
         _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), 1 if causal else 0, nseq, total_q, hq, hkv, d, bs, block_table.shape[1],
         nb, _code(q), _stream(stream)))
+
+
+def paged_attention_varlen_workspace_size(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                          block_size) -> int:
+    """Bytes of workspace paged_attention_varlen_split needs (0: none)."""
+    return int(lib().paged_attention_varlen_workspace_size(num_seqs, num_kv_heads, head_dim,
+                                                           max_blocks_per_seq, block_size))
+
+
+def paged_attention_varlen_split(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
+                                 causal=True, workspace=None, stream=None):
+    """paged_attention_varlen with long key ranges split over several
+    workgroups and merged exactly (workspace: uint8 on the GPU, or None for
+    the cached one of this stream)."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_gpu(n, t)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _need_gpu(n, t, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [total_q, Hq, D]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q/out dtype must match the pool")
+    nseq = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (nseq + 1,) or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q must be [num_seqs+1], block_table [num_seqs, max_blocks]")
+    total_q, hq, _ = q.shape
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_varlen_workspace_size(nseq, hkv, d, maxblk, bs) if total_q else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    else:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_varlen_split", lib().paged_attention_varlen_split(
+        _ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), 1 if causal else 0, nseq, total_q, hq, hkv, d, bs, maxblk, nb, _code(q),
+        _ptr(workspace), ws_bytes, _stream(s)))
 
 
 def paged_attention_varlen_ex(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,

@@ -51,7 +51,9 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
                            int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
-                           void* stream, const float* alibi, int32_t window_left, bool ext) {
+                           void* stream, const float* alibi, int32_t window_left, bool ext,
+                           void* workspace = nullptr, size_t workspace_bytes = 0,
+                           bool split = false) {
   if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
   if (dtype == PKV_F32) return PKV_ERR_DTYPE;  // matrix-core path: 16-bit inputs only
   if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
@@ -66,6 +68,15 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
     return PKV_ERR_NULL;
+  if (split) {
+    const size_t need = paged_attention_varlen_workspace_size(
+        num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    const int64_t wgs = pkv::varlen_tiles(total_q, num_seqs, num_q_heads / num_kv_heads) *
+                        pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits *
+                        num_kv_heads;
+    if (wgs > INT32_MAX) return PKV_ERR_SHAPE;
+  }
 
   pkv::VarlenArgs a;
   a.out = out;
@@ -87,8 +98,15 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
   a.dtype = dtype;
   a.alibi = alibi;
   a.window_left = window_left < 0 ? -1 : window_left;
-  hipError_t err = ext ? pkv::launch_varlen_ext(a, static_cast<hipStream_t>(stream))
-                       : pkv::launch_varlen(a, static_cast<hipStream_t>(stream));
+  if (split && workspace) {
+    const int64_t rows = (int64_t)pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits *
+                         num_seqs * num_kv_heads * pkv::kVlRowsWave;
+    a.ws_ml = static_cast<float*>(workspace);
+    a.ws_o = a.ws_ml + rows * 2;
+  }
+  hipError_t err = split ? pkv::launch_varlen_split(a, static_cast<hipStream_t>(stream))
+                   : ext ? pkv::launch_varlen_ext(a, static_cast<hipStream_t>(stream))
+                         : pkv::launch_varlen(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -222,6 +240,35 @@ int paged_attention_varlen_ex(void* out, const void* q, const int32_t* cu_seqlen
                      num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_blocks_per_seq, num_blocks, dtype, stream, alibi_slopes, window_left,
                      true);
+}
+
+// Workspace layout of the split varlen call: [S, B, Hkv, 32, 2] fp32 (max,
+// sum) and [S, B, Hkv, 32, D] fp32 partial outputs of the rows (at most one
+// wave's 32) of each sequence's last query tile per kv head; S = the most
+// chunks a tile of these sizes is cut into.
+size_t paged_attention_varlen_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq,
+                                             int32_t block_size) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return 0;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return 0;
+  const int64_t s = pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits;
+  if (s <= 1) return 0;
+  const int64_t rows = s * num_seqs * num_kv_heads * pkv::kVlRowsWave;
+  return (size_t)(rows * (2 + head_dim)) * sizeof(float);
+}
+
+int paged_attention_varlen_split(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, int causal,
+                                 int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return varlen_impl(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, causal,
+                     num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, dtype, stream, nullptr, -1, false, workspace,
+                     workspace_bytes, true);
 }
 
 int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -130,9 +130,45 @@ struct VarlenArgs {
   // variants: ALiBi slopes [Hq] fp32 (NULL = none), window (negative = none)
   const float* alibi = nullptr;
   int window_left = -1;
+  // split plan (workspace): [S, B, Hkv, 32, 2] (max in log2 units, sum) and
+  // [S, B, Hkv, 32, D] unnormalised outputs of the rows of cut tiles
+  float* ws_ml = nullptr;
+  float* ws_o = nullptr;
 };
+
+// Rows per workgroup of the packed prefill kernel (query positions x the
+// heads of a GQA group) and keys per KV tile.
+constexpr int kVlRows = 128;
+constexpr int kVlBN = 64;
+// Query tiles per kv head the grid provides: every sequence may end in a
+// partial tile.
+inline int64_t varlen_tiles(int64_t total_q, int num_seqs, int group) {
+  const int bq = kVlRows / group;
+  return (total_q + bq - 1) / bq + num_seqs;
+}
+// Split plan of the packed varlen call with a workspace: a query tile whose
+// rows fit one wave (a sequence's last, partial tile) and whose loop runs
+// over more key tiles than one chunk is cut into chunks of chunk_tiles key
+// tiles, each attended by its own workgroup; chunks hold at least
+// kVlChunkMin key tiles, and a tile is cut into at most kVlMaxSplits.
+constexpr int kVlChunkMin = 8;
+constexpr int kVlRowsWave = 32;   // query rows one wave of the prefill kernel owns
+constexpr int kVlMaxSplits = 16;
+struct VarlenSplit {
+  int chunk_tiles;
+  int max_splits;   // S: most chunks any tile of these sizes is cut into
+};
+inline VarlenSplit plan_varlen_split(int max_blocks_per_seq, int block_size) {
+  const long long wmax = ((long long)max_blocks_per_seq * block_size + kVlBN - 1) / kVlBN;
+  const long long ck = wmax > (long long)kVlChunkMin * kVlMaxSplits
+                           ? (wmax + kVlMaxSplits - 1) / kVlMaxSplits
+                           : kVlChunkMin;
+  const long long s = (wmax + ck - 1) / ck;
+  return {(int)ck, (int)(s > 1 ? s : 1)};
+}
 
 hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream);
 hipError_t launch_varlen_ext(const VarlenArgs& a, hipStream_t stream);
+hipError_t launch_varlen_split(const VarlenArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -26,9 +26,6 @@ namespace pkv {
 
 constexpr int kVlWaves = 4;
 constexpr int kVlThreads = kVlWaves * kWave;
-constexpr int kVlRows = 128;      // rows per workgroup = query positions x heads of the group
-constexpr int kVlRowsWave = 32;   // two 16-row MFMA tiles per wave
-constexpr int kVlBN = 64;         // keys per KV tile
 
 // K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
 // 16-byte slots: slot s of row r holds chunk s ^ f(r). The functions were
@@ -224,14 +221,36 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
 // EXT: the attention variants -- a sliding window (keys j >= p - window_left
 // for the query at p = i + Lk - Lq, window_left >= 0) and ALiBi (score +
 // alibi[h] * (j - p)); alibi may be NULL and window_left negative.
-template <class Ty, int D, bool EXT>
+// Chunks the split call cuts a query tile's key loop into: only a tile whose
+// rows fit one wave is cut -- a sequence's last, partial tile, such as a
+// decode row or the tail of a prefill -- into chunks of chunk_tiles key tiles
+// (full tiles already spread over many workgroups). (q0, lq, lk): the tile's
+// first query and the sequence's query and key counts.
+__device__ __forceinline__ int split_chunks(int q0, int lq, int lk, int bq, int group, int causal,
+                                            int chunk_tiles) {
+  const int nq = min(bq, lq - q0);
+  if (nq <= 0 || nq * group > kVlRowsWave) return 1;
+  const int kv_end = causal ? min(lk, q0 + nq + lk - lq) : lk;
+  const int w = kv_end > 0 ? (kv_end + kVlBN - 1) / kVlBN : 0;
+  return max(1, (w + chunk_tiles - 1) / chunk_tiles);
+}
+
+// SPLIT: the first n_tiles workgroup slots of each kv head are the tiles in
+// longest-first order with their chunk 0; after them num_seqs x
+// (max_splits - 1) slots take chunks 1 .. max_splits-1 of each sequence's
+// last tile (they exit when it is not cut that far): the heavy uncut tiles
+// start first and the short chunks fill in. A workgroup of a cut tile leaves
+// its rows' partial (max, sum, output) in its chunk's slot of the workspace
+// for the merge kernel.
+template <class Ty, int D, bool EXT, bool SPLIT>
 __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu_seqlens_q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2,
-    const float* __restrict__ alibi, int window_left) {
+    const float* __restrict__ alibi, int window_left, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o, int chunk_tiles, int max_splits, int n_tiles) {
   using L = VlLds<D>;
   constexpr int KS = D / 32;                 // k-steps of the QK product
   constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
@@ -252,7 +271,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // XCD serves fixed kv heads, whose K/V then stay in its L2 (with fewer kv
   // heads, a head's tiles alternate over the XCDs).
   const int kvh = blockIdx.x % num_kv_heads;
-  const int tile = blockIdx.x / num_kv_heads;
+  const int slot = blockIdx.x / num_kv_heads;
+  const bool extra = SPLIT && slot >= n_tiles;
+  const int tile = slot;
+  const int chunk = extra ? 1 + (slot - n_tiles) % (max_splits - 1) : 0;
+  const int xseq = extra ? (slot - n_tiles) / (max_splits - 1) : 0;
   const int group = num_q_heads / num_kv_heads;
   const int bq = kVlRows / group;   // query positions per tile
   const int bs = 1 << log2_bs;
@@ -271,12 +294,20 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     int seq = -1, q0 = 0, r0 = 0, lq_ = 0, lk_ = 0;
     // longest-first order; under a window a tile's key count is not
     // monotone in its position, so those tiles go by rank from the end
-    const bool found =
-        (EXT && window_left >= 0)
-            ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
-            : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
-                            max_blocks_per_seq << log2_bs, bq, causal, tile, lane, my_lq, my_lk,
-                            seq, q0);
+    bool found;
+    if (SPLIT && extra) {   // the last tile of sequence xseq
+      const int ntx = xseq < kWave ? __shfl(nt0, xseq, kWave)
+                                   : seq_tiles(cu_seqlens_q, num_seqs, bq, total_q, xseq);
+      found = ntx > 0;
+      seq = xseq;
+      q0 = (ntx - 1) * bq;
+    } else {
+      found = (EXT && window_left >= 0)
+                  ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
+                  : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
+                                  max_blocks_per_seq << log2_bs, bq, causal, tile, lane, my_lq,
+                                  my_lk, seq, q0);
+    }
     if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
       r0 = __shfl(my_r0, seq, kWave);
@@ -337,6 +368,16 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
   }
   const int kv_begin = windowed ? (max(0, q0 + delta - window_left) & ~(kVlBN - 1)) : 0;
+  // this workgroup's part of the key loop: [kv_lo, kv_hi)
+  int n_chunks = 1, kv_lo = kv_begin, kv_hi = kv_end;
+  if constexpr (SPLIT) {
+    n_chunks = split_chunks(q0, lq, lk, bq, group, causal, chunk_tiles);
+    if (chunk >= n_chunks) return;   // uniform over the workgroup
+    if (n_chunks > 1) {              // a tile that is not cut keeps its whole loop
+      kv_lo = kv_begin + chunk * chunk_tiles * kVlBN;
+      kv_hi = min(kv_end, kv_lo + chunk_tiles * kVlBN);
+    }
+  }
   const int mask_lo_end = windowed ? max(0, last_q + delta - window_left) : 0;
 
   const int row_stride = num_kv_heads * D;
@@ -415,7 +456,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
   };
 
-  if (kv_begin < kv_end) stage(0, kv_begin);
+  if (kv_lo < kv_hi) stage(0, kv_lo);
 
   // Q^T operands (B of S^T = K Q^T): lane holds Q[row][32s + 8*g4 .. +8]
   u32x4_t qb[2][KS];
@@ -462,9 +503,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const bool wave_live = __builtin_amdgcn_ballot_w64(row_ok[0] || row_ok[1]) != 0;
 
   int it = 0;
-  for (int kv0 = kv_begin; kv0 < kv_end; kv0 += kVlBN, ++it) {
+  for (int kv0 = kv_lo; kv0 < kv_hi; kv0 += kVlBN, ++it) {
     const int cur = it & 1;
-    const bool more = kv0 + kVlBN < kv_end;
+    const bool more = kv0 + kVlBN < kv_hi;
     if (more) stage(cur ^ 1, kv0 + kVlBN);
     // this tile's copies (issued one iteration earlier) have landed in LDS;
     // the next tile's stay in flight
@@ -616,6 +657,25 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     barrier_lds_ops();   // every wave is done with this stage before it is refilled
   }
 
+  if (SPLIT && n_chunks > 1) {
+    // partial triple of this chunk (o and the row sum relative to 2^m_use)
+    // for the rows of a cut tile, all in wave 0: slot [chunk, b, kv head, row]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (!row_ok[mt]) continue;
+      const int r = wave * kVlRowsWave + mt * 16 + l16;
+      const size_t slot_i =
+          (((size_t)chunk * num_seqs + b) * num_kv_heads + kvh) * kVlRowsWave + r;
+      float* o = ws_o + slot_i * D + 4 * g4;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) *reinterpret_cast<f32x4_t*>(o + 16 * nd) = acc[mt][nd];
+      if (g4 == 0) {
+        ws_ml[slot_i * 2 + 0] = m_use[mt];
+        ws_ml[slot_i * 2 + 1] = lacc[mt][0];
+      }
+    }
+    return;
+  }
   // ---- normalise and store: lane holds O^T[16nd + 4*g4 + i][row] ----
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -633,39 +693,101 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   }
 }
 
-template <class Ty, int D, bool EXT>
+// Exact merge of the chunk triples of the cut tiles, as the decode reduce:
+// M = max m_c, L = sum l_c 2^(m_c - M), out = sum o_c 2^(m_c - M) / L. One
+// workgroup per (sequence, kv head) recomputes the cut of the sequence's last
+// tile from its lengths (as the attention kernel did) and merges its rows; a
+// thread owns 4 consecutive output elements of a row.
+template <class Ty, int D>
+__global__ __launch_bounds__(256) void varlen_merge_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_lens, int num_seqs,
+    int total_q, int num_q_heads, int num_kv_heads, int max_lk, int causal, int chunk_tiles,
+    int max_splits) {
+  constexpr int TPP = D / 4;      // threads per row
+  constexpr int RPP = 256 / TPP;  // rows per pass
+  const int s = blockIdx.x / num_kv_heads, kvh = blockIdx.x % num_kv_heads;
+  const int group = num_q_heads / num_kv_heads, bq = kVlRows / group;
+  const int r0 = max(0, min(cu[s], total_q));
+  const int lq = max(0, min(cu[s + 1], total_q) - r0);
+  const int lk = max(0, min(seq_lens[s], max_lk));
+  if (lq <= 0) return;
+  const int q0 = (lq - 1) / bq * bq;   // the last tile
+  const int n = min(split_chunks(q0, lq, lk, bq, group, causal, chunk_tiles), max_splits);
+  if (n <= 1) return;
+  const int rows = min(bq, lq - q0) * group;
+  const int d0 = (threadIdx.x % TPP) * 4;
+  for (int r = threadIdx.x / TPP; r < rows; r += RPP) {
+    auto slot_i = [&](int c) {
+      return (((size_t)c * num_seqs + s) * num_kv_heads + kvh) * kVlRowsWave + r;
+    };
+    float mm = -INFINITY;
+    for (int c = 0; c < n; ++c) mm = fmaxf(mm, ws_ml[slot_i(c) * 2]);
+    const float mr = safe_max_ref(mm);
+    float ll = 0.f;
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c) {
+      const float wt = fast_exp2(ws_ml[slot_i(c) * 2] - mr);
+      ll += ws_ml[slot_i(c) * 2 + 1] * wt;
+      a += *reinterpret_cast<const f32x4_t*>(ws_o + slot_i(c) * D + d0) * wt;
+    }
+    const float inv = ll > 0.f ? 1.f / ll : 0.f;
+    u32x2_t w;
+    w[0] = Mma<Ty>::pack(a[0] * inv, a[1] * inv);
+    w[1] = Mma<Ty>::pack(a[2] * inv, a[3] * inv);
+    const int i = r / group, head = kvh * group + r % group;
+    *reinterpret_cast<u32x2_t*>(out + ((size_t)(r0 + q0 + i) * num_q_heads + head) * D + d0) = w;
+  }
+}
+
+template <class Ty, int D, bool EXT, bool SPLIT>
 static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int bq = kVlRows / group;
-  const int64_t tiles = (a.total_q + bq - 1) / bq + a.num_seqs;
+  const int64_t tiles = varlen_tiles(a.total_q, a.num_seqs, a.num_q_heads / a.num_kv_heads);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)a.head_dim);
-  dim3 grid((unsigned)(tiles * a.num_kv_heads));
-  launch_kernel((varlen_prefill_kernel<Ty, D, EXT>), grid, dim3(kVlThreads), 0, stream,
-                     static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
-                     a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
-                     static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens,
-                     a.causal, a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
-                     __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks,
-                     scale_log2, a.alibi, a.window_left);
+  const VarlenSplit sp = SPLIT ? plan_varlen_split(a.max_blocks_per_seq, a.block_size)
+                               : VarlenSplit{1, 1};
+  const int64_t extra = SPLIT ? (int64_t)a.num_seqs * (sp.max_splits - 1) : 0;
+  dim3 grid((unsigned)((tiles + extra) * a.num_kv_heads));
+  launch_kernel((varlen_prefill_kernel<Ty, D, EXT, SPLIT>), grid, dim3(kVlThreads), 0, stream,
+                static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
+                a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
+                static_cast<const uint16_t*>(a.v_cache), a.block_table, a.seq_lens, a.causal,
+                a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
+                __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks, scale_log2,
+                a.alibi, a.window_left, a.ws_ml, a.ws_o, sp.chunk_tiles, sp.max_splits,
+                (int)tiles);
+  hipError_t err = hipGetLastError();
+  if (!SPLIT || err != hipSuccess) return err;
+  launch_kernel((varlen_merge_kernel<Ty, D>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
+                dim3(256), 0, stream, static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o,
+                a.cu_seqlens_q, a.seq_lens, a.num_seqs, (int)a.total_q, a.num_q_heads,
+                a.num_kv_heads, a.max_blocks_per_seq * a.block_size, a.causal, sp.chunk_tiles,
+                sp.max_splits);
   return hipGetLastError();
 }
 
-template <bool EXT>
+template <bool EXT, bool SPLIT>
 static hipError_t launch_varlen_any(const VarlenArgs& a, hipStream_t stream) {
   if (a.dtype == 1) {
-    return a.head_dim == 64 ? launch_varlen_t<F16, 64, EXT>(a, stream)
-                            : launch_varlen_t<F16, 128, EXT>(a, stream);
+    return a.head_dim == 64 ? launch_varlen_t<F16, 64, EXT, SPLIT>(a, stream)
+                            : launch_varlen_t<F16, 128, EXT, SPLIT>(a, stream);
   }
-  return a.head_dim == 64 ? launch_varlen_t<BF16, 64, EXT>(a, stream)
-                          : launch_varlen_t<BF16, 128, EXT>(a, stream);
+  return a.head_dim == 64 ? launch_varlen_t<BF16, 64, EXT, SPLIT>(a, stream)
+                          : launch_varlen_t<BF16, 128, EXT, SPLIT>(a, stream);
 }
 
 hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
-  return launch_varlen_any<false>(a, stream);
+  return launch_varlen_any<false, false>(a, stream);
 }
 
 hipError_t launch_varlen_ext(const VarlenArgs& a, hipStream_t stream) {
-  return launch_varlen_any<true>(a, stream);
+  return launch_varlen_any<true, false>(a, stream);
+}
+
+hipError_t launch_varlen_split(const VarlenArgs& a, hipStream_t stream) {
+  if (plan_varlen_split(a.max_blocks_per_seq, a.block_size).max_splits <= 1)
+    return launch_varlen_any<false, false>(a, stream);
+  return launch_varlen_any<false, true>(a, stream);
 }
 
 }  // namespace pkv

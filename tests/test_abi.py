@@ -148,6 +148,44 @@ def test_varlen_validation(L):
     assert varlen(L, tq=0, q=None) == PKV_OK
 
 
+def varlen_split(L, ws=FAKE, wsb=1 << 40, **kw):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, causal=1, b=2, tq=100,
+             hq=8, hkv=2, d=128, bs=128, maxblk=32, nb=64, dtype=2)
+    a.update(kw)
+    return L.paged_attention_varlen_split(a["out"], a["q"], a["cu"], a["k"], a["v"], a["bt"],
+                                          a["sl"], a["causal"], a["b"], a["tq"], a["hq"],
+                                          a["hkv"], a["d"], a["bs"], a["maxblk"], a["nb"],
+                                          a["dtype"], ws, wsb, None)
+
+
+def test_varlen_split_workspace_size(L):
+    f = L.paged_attention_varlen_workspace_size
+    # 4096-token contexts: 64 key tiles -> chunks of 8 key tiles, at most 8
+    # per tile; (max, sum) + 128 outputs fp32 for 32 rows per (seq, kv head)
+    assert f(32, 8, 128, 256, 16) == 8 * 32 * 8 * 32 * (2 + 128) * 4
+    # 131072-token contexts: 2048 key tiles -> 16 chunks of 128 key tiles
+    assert f(4, 8, 64, 1024, 128) == 16 * 4 * 8 * 32 * (2 + 64) * 4
+    # contexts of at most 512 keys are never cut
+    assert f(32, 8, 128, 32, 16) == 0
+    assert f(0, 8, 128, 256, 16) == 0
+    assert f(32, 8, 96, 256, 16) == 0
+    assert f(32, 8, 128, 256, 8) == 0
+
+
+def test_varlen_split_validation(L):
+    need = L.paged_attention_varlen_workspace_size(2, 2, 128, 32, 128)
+    assert need > 0
+    assert varlen_split(L, ws=None) == PKV_ERR_WORKSPACE
+    assert varlen_split(L, wsb=need - 1) == PKV_ERR_WORKSPACE
+    assert varlen_split(L, dtype=0) == PKV_ERR_DTYPE
+    assert varlen_split(L, hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert varlen_split(L, d=256) == PKV_ERR_UNSUPPORTED
+    assert varlen_split(L, cu=None) == PKV_ERR_NULL
+    assert varlen_split(L, tq=0, q=None, ws=None) == PKV_OK
+    # contexts too short to cut need no workspace
+    assert L.paged_attention_varlen_workspace_size(2, 2, 128, 4, 128) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     if not os.path.exists(binding.library_path()):
