@@ -405,10 +405,38 @@ def main():
             if c == 6:
                 extra[m.name]["kv_gbs"] = round(m.kv_bytes_read() / (mu * 1e-3) / 1e9, 1)
                 extra[m.name]["kv_bytes"] = m.kv_bytes_read()
+                # the same batch through the split call (workspace from the binding's cache)
+                ms, _ = time_calls(lambda: binding.paged_attention_varlen_split(
+                    out, q, cu, k, v, bt, sl, True), n_extra)
+                mus = statistics.mean(ms)
+                extra[m.name]["split_us"] = round(mus * 1e3, 2)
+                extra[m.name]["split_kv_gbs"] = round(m.kv_bytes_read() / (mus * 1e-3) / 1e9, 1)
             if c == 4:
                 result["prefill_tflops"] = extra[m.name]["tflops"]
             del k, v, q, out
             torch.cuda.empty_cache()
+        # mixed batch over long contexts: 8 decode rows at 32768 tokens and two
+        # 512-query chunks over 2048 keys (32/8 heads, D 128, bs 16, bf16),
+        # plain call vs split call
+        m = wl.varlen_case(1007, [1] * 8 + [512, 512], [32768] * 8 + [2048, 2048], 32, 8, 128,
+                           16, "bf16", causal=True, values=False, name="mixed_long_decode_32k_bf16")
+        dtp = tdt(m.dtype)
+        k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
+        v = torch.randn_like(k)
+        q = torch.randn(int(m.cu_seqlens_q[-1]), m.num_q_heads, m.head_dim, dtype=dtp, device=dev)
+        out = torch.empty_like(q)
+        cu, bt, sl = ints(m.cu_seqlens_q), ints(m.block_table), ints(m.seq_lens)
+        ms, _ = time_calls(lambda: binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True),
+                           n_extra)
+        msx, _ = time_calls(lambda: binding.paged_attention_varlen_split(
+            out, q, cu, k, v, bt, sl, True), n_extra)
+        mu, mus = statistics.mean(ms), statistics.mean(msx)
+        extra[m.name] = {"us": round(mu * 1e3, 2), "split_us": round(mus * 1e3, 2),
+                         "kv_gbs": round(m.kv_bytes_read() / (mu * 1e-3) / 1e9, 1),
+                         "split_kv_gbs": round(m.kv_bytes_read() / (mus * 1e-3) / 1e9, 1),
+                         "kv_bytes": m.kv_bytes_read(), "flops": m.prefill_flops()}
+        del k, v, q, out
+        torch.cuda.empty_cache()
         # variants: ALiBi + a sliding window. Decode on the LLaMA-7B shape
         # (window 1024: bytes = the visible keys' rows), packed prefill of
         # workload 4 (window 512: flops = allowed pairs)
