@@ -267,6 +267,24 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const int l16 = lane & 15, g4 = lane >> 4;
   const int lrow = lane / CPR, lch = lane % CPR;
   const int bs = 1 << log2_bs;
+  static_assert(NT >= kMaxPartTokens / 16, "one block id per thread");
+
+  // The context length, the partition's block ids (every entry a full
+  // partition would use; those past the context are never read) and the
+  // queries depend only on the workgroup's indices: they are fetched in one
+  // round trip.
+  const int first_blk = (p * part_tokens) >> log2_bs;
+  const int nblk_max = min(part_tokens >> log2_bs, max_blocks_per_seq - first_blk);
+  const int id_raw =
+      tid < nblk_max ? block_table[(size_t)b * max_blocks_per_seq + first_blk + tid] : -1;
+  // queries as the B operand: lane holds head h0 + l16, dims 32s + 8*g4 .. +8
+  const bool head_ok = l16 < heads_per_wg;
+  u32x4_t qb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qb[s] = head_ok ? load16<false>(q + ((size_t)b * num_q_heads + h0 + l16) * D + 32 * s + 8 * g4)
+                    : u32x4_t{0u, 0u, 0u, 0u};
+  }
 
   int ctx = context_lens[b];
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
@@ -287,19 +305,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const int nparts_b = (ctx + part_tokens - 1) / part_tokens;
 
   const int nblk = (ntok + bs - 1) >> log2_bs;
-  for (int i = tid; i < nblk; i += NT) {
-    const int id = block_table[(size_t)b * max_blocks_per_seq + (part_start >> log2_bs) + i];
-    s_blk[i] = (id >= 0 && id < num_blocks) ? id : -1;
-  }
-
-  // queries as the B operand: lane holds head h0 + l16, dims 32s + 8*g4 .. +8
-  const bool head_ok = l16 < heads_per_wg;
-  u32x4_t qb[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qb[s] = head_ok ? load16<false>(q + ((size_t)b * num_q_heads + h0 + l16) * D + 32 * s + 8 * g4)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-  }
+  if (tid < nblk) s_blk[tid] = (id_raw >= 0 && id_raw < num_blocks) ? id_raw : -1;
   __syncthreads();
 
   const int row_stride = num_kv_heads * D;
