@@ -24,11 +24,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(uint4* __restrict__ k_cac
   if (gid >= num_pieces) return;
   const int64_t t = gid / pieces_per_row;
   const int piece = (int)(gid - t * pieces_per_row);
+  // the new rows are read together with their slot (one round trip), also
+  // for a skipped slot: those reads stay inside key / value
+  const uint4 kk = key[gid];
+  const uint4 vv = value[gid];
   const int32_t slot = slot_mapping[t];
   if (slot < 0 || (int64_t)slot >= num_slots) return;
   const int64_t dst = (int64_t)slot * pieces_per_row + piece;
-  const uint4 kk = key[gid];
-  const uint4 vv = value[gid];
   k_cache[dst] = kk;
   v_cache[dst] = vv;
 }
@@ -122,12 +124,15 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(
   if (gid >= num_pieces) return;
   const int64_t t = gid / pieces_per_row;
   const int piece = (int)(gid - t * pieces_per_row);
+  // codes are made while the slot is read (one round trip for both)
+  const int head = piece / pieces_per_head;
+  const uint4 kq = quantize16<Ty>(key + gid * 16, k_scale[head]);
+  const uint4 vq = quantize16<Ty>(value + gid * 16, v_scale[head]);
   const int32_t slot = slot_mapping[t];
   if (slot < 0 || (int64_t)slot >= num_slots) return;
-  const int head = piece / pieces_per_head;
   const int64_t dst = (int64_t)slot * pieces_per_row + piece;
-  k_cache[dst] = quantize16<Ty>(key + gid * 16, k_scale[head]);
-  v_cache[dst] = quantize16<Ty>(value + gid * 16, v_scale[head]);
+  k_cache[dst] = kq;
+  v_cache[dst] = vq;
 }
 
 hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, const void* value,
