@@ -721,15 +721,31 @@ __global__ __launch_bounds__(256) void varlen_merge_kernel(
     auto slot_i = [&](int c) {
       return (((size_t)c * num_seqs + s) * num_kv_heads + kvh) * kVlRowsWave + r;
     };
+    // every chunk's triple is loaded before any is used (one round trip)
+    float mc[kVlMaxSplits], lc[kVlMaxSplits];
+    f32x4_t oc[kVlMaxSplits];
+#pragma unroll
+    for (int c = 0; c < kVlMaxSplits; ++c) {
+      mc[c] = -INFINITY;
+      lc[c] = 0.f;
+      oc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (c < n) {
+        mc[c] = ws_ml[slot_i(c) * 2];
+        lc[c] = ws_ml[slot_i(c) * 2 + 1];
+        oc[c] = *reinterpret_cast<const f32x4_t*>(ws_o + slot_i(c) * D + d0);
+      }
+    }
     float mm = -INFINITY;
-    for (int c = 0; c < n; ++c) mm = fmaxf(mm, ws_ml[slot_i(c) * 2]);
+#pragma unroll
+    for (int c = 0; c < kVlMaxSplits; ++c) mm = fmaxf(mm, mc[c]);
     const float mr = safe_max_ref(mm);
     float ll = 0.f;
     f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < n; ++c) {
-      const float wt = fast_exp2(ws_ml[slot_i(c) * 2] - mr);
-      ll += ws_ml[slot_i(c) * 2 + 1] * wt;
-      a += *reinterpret_cast<const f32x4_t*>(ws_o + slot_i(c) * D + d0) * wt;
+#pragma unroll
+    for (int c = 0; c < kVlMaxSplits; ++c) {
+      const float wt = c < n ? fast_exp2(mc[c] - mr) : 0.f;
+      ll += lc[c] * wt;
+      a += oc[c] * wt;
     }
     const float inv = ll > 0.f ? 1.f / ll : 0.f;
     u32x2_t w;
