@@ -201,8 +201,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
 
 // ---------------------------------------------------------------------------
 // Matrix-core decode (fp16 / bf16). One workgroup per (partition, group of up
-// to 16 query heads sharing a kv head, sequence); each of its WAVES waves owns
-// a contiguous share of the partition and walks it TT tokens at a time.
+// to 16 query heads sharing a kv head, sequence); its WAVES waves walk the
+// partition TT tokens (one tile) at a time, taking tiles on demand.
 //
 // K and V rows are fetched exactly as in the vector kernel (16 lanes x 16 B
 // per 256-byte row, non-temporal) into registers, one tile ahead, and parked
@@ -236,7 +236,7 @@ struct MfLds {
 // only, window_left >= 0) and ALiBi (score + alibi[h] * (j - (ctx-1)));
 // alibi may be NULL and window_left negative. Positions are those of the
 // decode query, the last token of its context.
-template <class Ty, int D, int WAVES, int TT, int PD, bool Q8, bool EXT>
+template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
@@ -258,6 +258,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
   __shared__ __attribute__((aligned(16))) uint8_t s_mem[L::bytes];
   __shared__ int s_blk[kMaxPartTokens / 16];
+  __shared__ int s_claim;   // next tile to hand out
 
   const int p = blockIdx.x;
   const int h0 = blockIdx.y * heads_per_wg;
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
   const int nblk = (ntok + bs - 1) >> log2_bs;
   if (tid < nblk) s_blk[tid] = (id_raw >= 0 && id_raw < num_blocks) ? id_raw : -1;
+  if (tid == 0) s_claim = WAVES;
   __syncthreads();
 
   const int row_stride = num_kv_heads * D;
@@ -318,29 +320,37 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const float al2 = (EXT && alibi != nullptr && head_ok) ? alibi[h0 + l16] * 1.4426950408889634f
                                                          : 0.f;
   const int lo_local = lo - part_start;
-  // waves own contiguous, TT-aligned shares of [tb, ntok)
-  const int share = ((ntok - tb + WAVES * TT - 1) / (WAVES * TT)) * TT;
-  const int wtok0 = tb + wave * share;
-  const int wtok_n = max(0, min(ntok - wtok0, share));
-  const int niter = (wtok_n + TT - 1) / TT;
+  // Tiles g = 0 .. ntiles-1 cover local tokens [tb + g*TT, tb + (g+1)*TT).
+  // Wave w starts on tile w and claims each further tile from a counter in
+  // LDS as it issues that tile's loads. (With fixed equal shares the second
+  // wave of each SIMD, which loses issue arbitration to the first, finished
+  // several microseconds after it; on demand the waves end within about a
+  // tile of each other.) A wave's set of tiles, and so the rounding of its
+  // partial sums, varies from call to call.
+  const int ntiles = (ntok - tb + TT - 1) / TT;
   const int last_grp = (ntok - 1) & ~(RPI - 1);
 
   uint8_t* s_k = s_mem + wave * L::waveB;
   uint8_t* s_v = s_k + L::tileB;
 
-  // register ring of PD tiles: tile it+PD is fetched while tile it is used
-  u32x4_t kr[PD][LPI], vr[PD][LPI];
-  auto fetch = [&](int it, u32x4_t (&kk)[LPI], u32x4_t (&vv)[LPI]) {
+  // the next tile is fetched into registers while the current one is used
+  u32x4_t kr[LPI], vr[LPI];
+  auto fetch = [&](int g) {
 #pragma unroll
     for (int j = 0; j < LPI; ++j) {
-      const int t0 = wtok0 + it * TT + j * RPI;           // first row of this load (uniform)
+      const int t0 = tb + g * TT + j * RPI;               // first row of this load (uniform)
       const int tg = min(t0, last_grp);                    // groups past the end re-read the last
       const int tok = min(tg + lrow, ntok - 1);
       const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
       const size_t off = (((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off) * EB;
-      kk[j] = load16<true>(kbytes + off);
-      vv[j] = load16<true>(vbytes + off);
+      kr[j] = load16<true>(kbytes + off);
+      vr[j] = load16<true>(vbytes + off);
     }
+  };
+  auto claim = [&]() {   // wave-uniform
+    int g = 0;
+    if (lane == 0) g = atomicAdd(&s_claim, 1);
+    return __builtin_amdgcn_readfirstlane(g);
   };
 
   f32x4_t acc[ND];
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   // dims 16nd + 4*(i%4) .. +4, and receives dim 16nd + i of tokens 4*g4 .. +4
   const uint8_t* vt = s_v + (4 * g4 + (l16 >> 2)) * L::rowB + (l16 & 3) * 8;
 
-  auto tile = [&](int it) {
+  auto tile = [&](int g) {
     f32x4_t st[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       }
     }
     // lane holds tokens 16n + 4*g4 + i of this tile for head l16
-    const int tbase = wtok0 + it * TT + 4 * g4;
+    const int tbase = tb + g * TT + 4 * g4;
     // distance of the lane's first token to the query (ALiBi)
     const float dj0 = (float)(part_start + tbase - (ctx - 1));
     float sv[NS][4];
@@ -421,35 +431,31 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
   };
 
+  int g = wave;
+  if (g < ntiles) fetch(g);
+  while (g < ntiles) {
+    // park tile g in the wave's LDS tile (later LDS reads of this wave see it)
 #pragma unroll
-  for (int u = 0; u < PD; ++u)
-    if (u < niter) fetch(u, kr[u], vr[u]);
-  for (int it0 = 0; it0 < niter; it0 += PD) {
-#pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int it = it0 + u;
-      if (it < niter) {
-#pragma unroll
-        for (int j = 0; j < LPI; ++j) {
-          uint8_t* dk = s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
-          uint8_t* dv = s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
-          if constexpr (Q8) {
-            u32x4_t lo, hi;
-            widen_i8x16<Ty>(kr[u][j], lo, hi);
-            *reinterpret_cast<u32x4_t*>(dk) = lo;
-            *reinterpret_cast<u32x4_t*>(dk + 16) = hi;
-            widen_i8x16<Ty>(vr[u][j], lo, hi);
-            *reinterpret_cast<u32x4_t*>(dv) = lo;
-            *reinterpret_cast<u32x4_t*>(dv + 16) = hi;
-          } else {
-            *reinterpret_cast<u32x4_t*>(dk) = kr[u][j];
-            *reinterpret_cast<u32x4_t*>(dv) = vr[u][j];
-          }
-        }
-        if (it + PD < niter) fetch(it + PD, kr[u], vr[u]);
-        tile(it);
+    for (int j = 0; j < LPI; ++j) {
+      uint8_t* dk = s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+      uint8_t* dv = s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+      if constexpr (Q8) {
+        u32x4_t lo, hi;
+        widen_i8x16<Ty>(kr[j], lo, hi);
+        *reinterpret_cast<u32x4_t*>(dk) = lo;
+        *reinterpret_cast<u32x4_t*>(dk + 16) = hi;
+        widen_i8x16<Ty>(vr[j], lo, hi);
+        *reinterpret_cast<u32x4_t*>(dv) = lo;
+        *reinterpret_cast<u32x4_t*>(dv + 16) = hi;
+      } else {
+        *reinterpret_cast<u32x4_t*>(dk) = kr[j];
+        *reinterpret_cast<u32x4_t*>(dv) = vr[j];
       }
     }
+    const int gn = claim();
+    if (gn < ntiles) fetch(gn);
+    tile(g);
+    g = gn;
   }
 
   // ---- merge lanes (the 4 lane groups) and waves ----
@@ -599,7 +605,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
 }
 
-template <class Ty, int D, int WAVES, int TT, int PD, bool Q8, bool EXT>
+template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT>
 static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
                                   int part_tokens) {
   const int log2_bs = __builtin_ctz(a.block_size);
@@ -607,7 +613,7 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, PD, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
+  launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
                      stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
                      scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw, log2_bs,
@@ -627,8 +633,8 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
                                       a.block_size);
   if (plan.waves == 8)
-    return launch_mfma_cfg<Ty, D, 8, 32, 1, Q8, EXT>(a, stream, hpw, plan.part_tokens);
-  return launch_mfma_cfg<Ty, D, 4, 16, 1, Q8, EXT>(a, stream, hpw, plan.part_tokens);
+    return launch_mfma_cfg<Ty, D, 8, 32, Q8, EXT>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16, Q8, EXT>(a, stream, hpw, plan.part_tokens);
 }
 
 template <int D>
