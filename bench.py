@@ -216,8 +216,11 @@ def main():
     new_slots = ints(meta.slot_mapping[meta.new_token_rows])
 
     def step():
-        binding.paged_kv_write(t["k"], t["v"], new_key, new_val, new_slots)
-        run_decode(meta, t)
+        """One decode step through the fused call: the new tokens are written
+        and attended in one launch (paged_kv_write_decode)."""
+        binding.paged_kv_write_decode(t["out"], t["q"], t["k"], t["v"], new_key, new_val,
+                                      new_slots, t["bt"], t["ctx"], meta.block_size, meta.scale,
+                                      workspace=t["ws"])
 
     def kernel_pass(fn, n):
         """ms of the first kernel of each of n calls, from events the kernel
@@ -240,28 +243,44 @@ def main():
     wall0 = time.perf_counter()
     for i in range(args.steps):
         evict()
-        e0, e1, e2 = tm.ev[i]
+        e0, e1, _ = tm.ev[i]
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b, _ in tm.ev]
+    # kernel-level pass right after the timed steps, same inputs and cache
+    # flush: the fused kernel records dispatch events (arming them makes the
+    # runtime add gaps around the call, so the timed steps run unarmed)
+    kern_ms = kernel_pass(step, args.steps)
+    kern_mean = statistics.mean(kern_ms)
+    e = wl.ELEM_BYTES[meta.dtype]
+    # the step reads every context token's K/V once (the new token's from
+    # key/value), q, the live table entries, the lengths and the slots, and
+    # writes out and the new rows
+    new_rows_bytes = 2 * meta.num_seqs * meta.num_kv_heads * meta.head_dim * e
+    step_bytes = meta.decode_bytes() + new_rows_bytes + 4 * meta.num_seqs
+    kern_gbs = step_bytes / (kern_mean * 1e-3) / 1e9
+    ms_per_step = statistics.mean(step_ms)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # for comparison: the same step as two calls (paged_kv_write, then
+    # paged_attention_decode), and the decode call's own kernel
+    tm2 = Timer(torch, args.steps)
+    for i in range(args.steps):
+        evict()
+        e0, e1, e2 = tm2.ev[i]
         e0.record()
         binding.paged_kv_write(t["k"], t["v"], new_key, new_val, new_slots)
         e1.record()
         run_decode(meta, t)
         e2.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = [a.elapsed_time(c) for a, b, c in tm.ev]
-    dec_ms = [b.elapsed_time(c) for a, b, c in tm.ev]
-    write_ms = [a.elapsed_time(b) for a, b, c in tm.ev]
-    # kernel-level pass right after the timed steps, same inputs and cache
-    # flush: the decode kernel records dispatch events (arming them makes the
-    # runtime add gaps around the call, so the timed steps run unarmed)
-    kern_ms = kernel_pass(lambda: run_decode(meta, t), args.steps)
-    kern_mean = statistics.mean(kern_ms)
-    kern_gbs = meta.decode_bytes() / (kern_mean * 1e-3) / 1e9
-    ms_per_step = statistics.mean(step_ms)
-    e = wl.ELEM_BYTES[meta.dtype]
-    write_bytes = 2 * 2 * meta.num_seqs * meta.num_kv_heads * meta.head_dim * e + 4 * meta.num_seqs
-    step_bytes = meta.decode_bytes() + write_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    two_ms = [a.elapsed_time(c) for a, b, c in tm2.ev]
+    dec_ms = [b.elapsed_time(c) for a, b, c in tm2.ev]
+    write_ms = [a.elapsed_time(b) for a, b, c in tm2.ev]
+    dec_kern_ms = kernel_pass(lambda: run_decode(meta, t), args.steps)
     dec_mean = statistics.mean(dec_ms)
     dec_gbs = meta.decode_bytes() / (dec_mean * 1e-3) / 1e9
 
@@ -279,7 +298,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic: N(0,1) fp16 K/V/q, seeded random block permutation, inputs resident in HBM",
         "config": {"workload": "llama7b-shaped paged decode step: write 1 new token/seq via "
-                               "slot_mapping, then decode", "batch": meta.num_seqs,
+                               "slot_mapping and decode, one fused call", "batch": meta.num_seqs,
                    "context": int(meta.seq_lens[0]), "q_heads": meta.num_q_heads,
                    "kv_heads": meta.num_kv_heads, "head_dim": meta.head_dim,
                    "block_size": meta.block_size, "pool_blocks": meta.num_blocks,
@@ -291,28 +310,32 @@ def main():
         "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
                                 round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "step_kernel_us": round(kern_mean * 1e3, 2),
+        "step_kernel_us_median": round(statistics.median(kern_ms) * 1e3, 2),
+        "step_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                                   round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
+        "two_call_us_per_step": round(statistics.mean(two_ms) * 1e3, 2),
+        "kv_write_call_us": round(statistics.mean(write_ms) * 1e3, 2),
         "decode_call_us": round(dec_mean * 1e3, 2),
         "decode_call_gbs": round(dec_gbs, 1),
-        "decode_kernel_us": round(kern_mean * 1e3, 2),
-        "decode_kernel_us_median": round(statistics.median(kern_ms) * 1e3, 2),
-        "decode_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
-                                     round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
-        "kv_write_call_us": round(statistics.mean(write_ms) * 1e3, 2),
+        "decode_kernel_us": round(statistics.mean(dec_kern_ms) * 1e3, 2),
+        "decode_kernel_gbs": round(meta.decode_bytes() / statistics.mean(dec_kern_ms) / 1e6, 1),
         "step_bytes": step_bytes,
         "timed_wall_s": round(wall, 4),
     }
     traffic, trec = measured_traffic()
     result["roofline"] = {
-        "kernel": "decode_mfma_kernel (one launch per paged_attention_decode call on this batch: "
-                  "8-wave workgroups, one whole 2048-token context each, no split)",
+        "kernel": "decode_mfma_kernel, fused-write instance (the one launch of a "
+                  "paged_kv_write_decode call on this batch: 8-wave workgroups, one whole "
+                  "2048-token context each, no split)",
         "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "algorithmic_bytes_per_launch": meta.decode_bytes(),
+        "algorithmic_bytes_per_launch": step_bytes,
         "timing": "per launch: HIP events recorded by the kernel dispatch itself "
                   "(hipExtLaunchKernel through pkv_time_next_kernel) on the launch stream, "
                   "mean over a pass of as many calls as timed steps that follows them "
                   "(same inputs, same cache flush); events around the whole call "
-                  "(decode_call_us) add the event-packet gaps",
+                  "(us_per_step) add the event-packet gaps",
     }
     if trec is not None:
         result["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_FILE, ROOT)

@@ -138,6 +138,40 @@ int paged_attention_decode(void* out, const void* q, const void* k_cache, const 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_kv_write_decode -- one decode step: the new token of every sequence
+ * is written into the pool (paged_kv_write) and then attended over
+ * (paged_attention_decode), in a single launch.
+ *
+ * Equivalent to paged_kv_write(k_cache, v_cache, key, value, slot_mapping,
+ * num_seqs, ...) followed by paged_attention_decode(...) on the same
+ * arguments, the sequence of the skill page's section 3.6 (the KV length
+ * includes the token just written). Token b of key/value is sequence b's
+ * new token and normally sits at its last position, context_lens[b] - 1:
+ * when slot_mapping[b] is the table's slot of that position, the attention
+ * takes the token's K/V from key/value directly (the values the write stores
+ * there), so no part of the call waits for the store. Precondition for the
+ * equivalence: no sequence of the call reads a slot written by the call
+ * other than at that position (a sequence's last block is its own).
+ * Rounding may differ from the two separate calls in the last bits.
+ *
+ *   out, q, block_table, context_lens, scale, workspace : as paged_attention_decode
+ *   k_cache, v_cache : the pool (written: the new rows)
+ *   key, value       : [num_seqs, num_kv_heads, head_dim], dtype
+ *   slot_mapping     : [num_seqs] int32; negative or >= num_blocks*block_size
+ *                      entries are skipped, as in paged_kv_write
+ *   workspace_bytes  : >= paged_attention_decode_workspace_size(...)
+ * Accepts dtype PKV_F32, PKV_F16, PKV_BF16 (for PKV_F32 the library runs the
+ * write and the decode as two launches).
+ */
+int paged_kv_write_decode(void* out, const void* q, void* k_cache, void* v_cache,
+                          const void* key, const void* value, const int32_t* slot_mapping,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          int32_t block_size, float scale, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_varlen -- packed variable-length (prefill) attention over
  * the paged cache.
  *

@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32,
                                              i32, i32, i32, i64, i32, vp, sz, vp]
         L.paged_attention_decode.restype = ctypes.c_int
+        L.paged_kv_write_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                            ctypes.c_float, i32, i32, i32, i32, i32, i64, i32,
+                                            vp, sz, vp]
+        L.paged_kv_write_decode.restype = ctypes.c_int
         L.paged_attention_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i64,
                                              i32, i32, i32, i32, i32, i64, i32, vp]
         L.paged_attention_varlen.restype = ctypes.c_int
@@ -224,6 +228,44 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens, 
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
         bs, float(scale), bsz, hq, hkv, d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes,
         _stream(s)))
+
+
+def paged_kv_write_decode(out, q, k_cache, v_cache, key, value, slot_mapping, block_table,
+                          context_lens, block_size, scale, workspace=None, stream=None):
+    """One decode step in one launch: key[b] / value[b] (sequence b's new
+    token) go to pool row slot_mapping[b], then out [B, Hq, D] attends over
+    context_lens[b] tokens (the new one included)."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("key", key), ("value", value)):
+        _need_gpu(n, t)
+    for n, t in (("slot_mapping", slot_mapping), ("block_table", block_table),
+                 ("context_lens", context_lens)):
+        _need_gpu(n, t, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [num_seqs, Hq, D]")
+    for t in (q, out, key, value):
+        if t.dtype != k_cache.dtype:
+            raise TypeError("q/out/key/value dtype must match the pool")
+    bsz, hq, _ = q.shape
+    if key.shape != (bsz, hkv, d) or value.shape != key.shape or slot_mapping.shape != (bsz,):
+        raise ValueError("key/value must be [num_seqs, Hkv, D], slot_mapping [num_seqs]")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_decode_workspace_size(bsz, hq, d, maxblk, bs) if bsz else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    elif need:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_kv_write_decode", lib().paged_kv_write_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
+        _ptr(slot_mapping), _ptr(block_table), _ptr(context_lens), bs, float(scale), bsz, hq, hkv,
+        d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes, _stream(s)))
 
 
 def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,

@@ -236,7 +236,17 @@ struct MfLds {
 // only, window_left >= 0) and ALiBi (score + alibi[h] * (j - (ctx-1)));
 // alibi may be NULL and window_left negative. Positions are those of the
 // decode query, the last token of its context.
-template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT>
+// APP: the decode step's KV write rides along (one launch instead of two).
+// new_k / new_v [B, Hkv, D] hold each sequence's new token, slot_mapping[b]
+// its pool slot (skipped when negative or past the pool). One workgroup per
+// (sequence, kv head) stores the row into the pool; every workgroup whose
+// partition holds the last position ctx-1 takes that token's K/V from
+// new_k / new_v instead of the pool when slot_mapping[b] is the table's slot
+// of ctx-1 -- the values the write stores there -- so no workgroup waits for
+// the store. The result equals the write followed by the decode as long as
+// no other sequence of the call reads that slot (a sequence's last block is
+// its own).
+template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT, bool APP>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
@@ -244,7 +254,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_o, float scale_log2, int num_q_heads,
     int num_kv_heads, int group, int heads_per_wg, int log2_bs, int max_blocks_per_seq,
     int64_t num_blocks, int num_parts, int part_tokens, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, const float* __restrict__ alibi, int window_left) {
+    const float* __restrict__ v_scale, const float* __restrict__ alibi, int window_left,
+    uint8_t* app_k_cache, uint8_t* app_v_cache, const void* __restrict__ new_k,
+    const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping) {
   using L = MfLds<D, WAVES, TT>;
   constexpr int NT = WAVES * kWave;
   constexpr int EB = Q8 ? 1 : 2;      // bytes per cached element
@@ -271,9 +283,22 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   static_assert(NT >= kMaxPartTokens / 16, "one block id per thread");
 
   // The context length, the partition's block ids (every entry a full
-  // partition would use; those past the context are never read) and the
-  // queries depend only on the workgroup's indices: they are fetched in one
-  // round trip.
+  // partition would use; those past the context are never read), the
+  // queries and (APP) the new token's row and slot depend only on the
+  // workgroup's indices: they are fetched in one round trip.
+  const int row_stride = num_kv_heads * D;
+  // APP: 2 x CPR threads of the kv head's first head group hold a 16-byte
+  // chunk of the new K (then V) row; the workgroup of the partition holding
+  // position ctx-1 (partition 0 for an empty context) stores it
+  const bool app_lane = APP && h0 == kvh * group && tid < 2 * CPR;
+  u32x4_t app_row = {0u, 0u, 0u, 0u};
+  if constexpr (APP) {
+    if (app_lane) {
+      const uint8_t* src = static_cast<const uint8_t*>(tid >= CPR ? new_v : new_k);
+      app_row = *reinterpret_cast<const u32x4_t*>(
+          src + ((size_t)b * row_stride + kvh * D + (tid % CPR) * EPC) * EB);
+    }
+  }
   const int first_blk = (p * part_tokens) >> log2_bs;
   const int nblk_max = min(part_tokens >> log2_bs, max_blocks_per_seq - first_blk);
   const int id_raw =
@@ -289,11 +314,23 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
   int ctx = context_lens[b];
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
+  const int app_slot = APP ? slot_mapping[b] : -1;
+  const int part_start = p * part_tokens;
+  auto app_store = [&]() {
+    if constexpr (APP) {
+      const int pw = ctx > 0 ? (ctx - 1) / part_tokens : 0;
+      if (app_lane && p == pw && app_slot >= 0 && (int64_t)app_slot < (num_blocks << log2_bs)) {
+        uint8_t* dst = tid >= CPR ? app_v_cache : app_k_cache;
+        *reinterpret_cast<u32x4_t*>(
+            dst + ((size_t)app_slot * row_stride + kvh * D + (tid % CPR) * EPC) * EB) = app_row;
+      }
+    }
+  };
   // visible keys [lo, ctx); loads start at lo16 (16-aligned: one block per load)
   const int lo = (EXT && window_left >= 0) ? max(0, ctx - 1 - window_left) : 0;
   const int lo16 = lo & ~15;
-  const int part_start = p * part_tokens;
   if (part_start >= ctx) {
+    app_store();   // an empty context: its new row is still stored
     if (p == 0) {
       for (int i = tid; i < heads_per_wg * D; i += NT)
         out[((size_t)b * num_q_heads + h0 + i / D) * D + i % D] = 0;
@@ -309,8 +346,18 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   if (tid < nblk) s_blk[tid] = (id_raw >= 0 && id_raw < num_blocks) ? id_raw : -1;
   if (tid == 0) s_claim = WAVES;
   __syncthreads();
+  app_store();
 
-  const int row_stride = num_kv_heads * D;
+  // local token whose K/V come from new_k / new_v (-1: none)
+  int app_pos = -1;
+  if constexpr (APP) {
+    const int last = ctx - 1 - part_start;
+    if (last >= 0 && last < ntok && app_slot >= 0) {
+      const int blk = s_blk[last >> log2_bs];
+      if (blk >= 0 && (int64_t)blk * bs + (last & (bs - 1)) == (int64_t)app_slot) app_pos = last;
+    }
+  }
+
   const int head_off = kvh * D + lch * EPC;
   const uint8_t* kbytes = static_cast<const uint8_t*>(k_cache);
   const uint8_t* vbytes = static_cast<const uint8_t*>(v_cache);
@@ -343,8 +390,18 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       const int tok = min(tg + lrow, ntok - 1);
       const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
       const size_t off = (((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off) * EB;
-      kr[j] = load16<true>(kbytes + off);
-      vr[j] = load16<true>(vbytes + off);
+      const uint8_t* kp = kbytes + off;
+      const uint8_t* vp = vbytes + off;
+      if constexpr (APP) {
+        // (uniform test first: this load's rows are tg .. tg+RPI-1, clamped)
+        if (app_pos >= tg && app_pos < tg + RPI && tok == app_pos) {
+          const size_t src = ((size_t)b * row_stride + head_off) * EB;
+          kp = static_cast<const uint8_t*>(new_k) + src;
+          vp = static_cast<const uint8_t*>(new_v) + src;
+        }
+      }
+      kr[j] = load16<true>(kp);
+      vr[j] = load16<true>(vp);
     }
   };
   auto claim = [&]() {   // wave-uniform
@@ -605,7 +662,7 @@ static hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, kDecodePart);
 }
 
-template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT>
+template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT, bool APP>
 static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int hpw,
                                   int part_tokens) {
   const int log2_bs = __builtin_ctz(a.block_size);
@@ -613,18 +670,20 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
-  launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, Q8, EXT>), grid, dim3(WAVES * kWave), 0,
+  launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, Q8, EXT, APP>), grid, dim3(WAVES * kWave), 0,
                      stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
                      scale_log2, a.num_q_heads, a.num_kv_heads, group, hpw, log2_bs,
                      a.max_blocks_per_seq, a.num_blocks, parts, part_tokens, a.k_scale,
-                     a.v_scale, a.alibi, a.window_left);
+                     a.v_scale, a.alibi, a.window_left, static_cast<uint8_t*>(a.app_k_cache),
+                     static_cast<uint8_t*>(a.app_v_cache), a.new_key, a.new_value,
+                     a.slot_mapping);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || parts <= 1) return err;
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
 }
 
-template <class Ty, int D, bool Q8 = false, bool EXT = false>
+template <class Ty, int D, bool Q8 = false, bool EXT = false, bool APP = false>
 static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   int hpw = 1;  // largest divisor of the group size that fits one 16-row tile
@@ -633,8 +692,8 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
                                       a.block_size);
   if (plan.waves == 8)
-    return launch_mfma_cfg<Ty, D, 8, 32, Q8, EXT>(a, stream, hpw, plan.part_tokens);
-  return launch_mfma_cfg<Ty, D, 4, 16, Q8, EXT>(a, stream, hpw, plan.part_tokens);
+    return launch_mfma_cfg<Ty, D, 8, 32, Q8, EXT, APP>(a, stream, hpw, plan.part_tokens);
+  return launch_mfma_cfg<Ty, D, 4, 16, Q8, EXT, APP>(a, stream, hpw, plan.part_tokens);
 }
 
 template <int D>
@@ -673,6 +732,23 @@ hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {
                : launch_decode_mfma<F16, 128, true>(a, stream);
   return d64 ? launch_decode_mfma<BF16, 64, true>(a, stream)
              : launch_decode_mfma<BF16, 128, true>(a, stream);
+}
+
+hipError_t launch_write_decode(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_dim == 64;
+  switch (a.dtype) {
+    case 0: {   // fp32 pool: the vector-ALU decode has no fused form; write, then decode
+      hipError_t err = launch_kv_write(a.app_k_cache, a.app_v_cache, a.new_key, a.new_value,
+                                       a.slot_mapping, a.num_seqs,
+                                       a.num_kv_heads * a.head_dim * 4,
+                                       a.num_blocks * a.block_size, stream);
+      return err != hipSuccess ? err : launch_decode(a, stream);
+    }
+    case 1: return d64 ? launch_decode_mfma<F16, 64, false, false, true>(a, stream)
+                       : launch_decode_mfma<F16, 128, false, false, true>(a, stream);
+    default: return d64 ? launch_decode_mfma<BF16, 64, false, false, true>(a, stream)
+                        : launch_decode_mfma<BF16, 128, false, false, true>(a, stream);
+  }
 }
 
 }  // namespace pkv

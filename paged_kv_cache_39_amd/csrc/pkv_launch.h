@@ -105,11 +105,21 @@ struct DecodeArgs {
   // variants: ALiBi slopes [Hq] fp32 (NULL = none), window (negative = none)
   const float* alibi = nullptr;
   int window_left = -1;
+  // fused KV write (launch_write_decode): the pool again, writable, and one
+  // new token per sequence: new_key / new_value [B, Hkv, D], slot_mapping [B]
+  void* app_k_cache = nullptr;
+  void* app_v_cache = nullptr;
+  const void* new_key = nullptr;
+  const void* new_value = nullptr;
+  const int32_t* slot_mapping = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // window / ALiBi variants, q/out of a.dtype (fp16 or bf16)
 hipError_t launch_decode_ext(const DecodeArgs& a, hipStream_t stream);
+// the decode step's KV write (one new token per sequence) and the decode in
+// one launch (fp16 / bf16; an fp32 pool takes the two kernels in turn)
+hipError_t launch_write_decode(const DecodeArgs& a, hipStream_t stream);
 // int8 cache (codes), q/out of a.dtype (fp16 or bf16)
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
 
