@@ -99,6 +99,33 @@ def test_decode_validation(L):
     assert decode(L, b=0, q=None) == PKV_OK                    # empty batch
 
 
+def write_decode(L, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, key=FAKE, value=FAKE, slots=FAKE, bt=FAKE,
+             ctx=FAKE, bs=16, scale=0.1, b=2, hq=8, hkv=2, d=128, maxblk=64, nb=256, dtype=2,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.paged_kv_write_decode(a["out"], a["q"], a["k"], a["v"], a["key"], a["value"],
+                                   a["slots"], a["bt"], a["ctx"], a["bs"], a["scale"], a["b"],
+                                   a["hq"], a["hkv"], a["d"], a["maxblk"], a["nb"], a["dtype"],
+                                   a["ws"], a["wsb"], None)
+
+
+def test_write_decode_validation(L):
+    assert write_decode(L, dtype=3) == PKV_ERR_DTYPE
+    assert write_decode(L, hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert write_decode(L, d=80) == PKV_ERR_UNSUPPORTED
+    assert write_decode(L, bs=8) == PKV_ERR_UNSUPPORTED
+    assert write_decode(L, maxblk=0) == PKV_ERR_SHAPE
+    assert write_decode(L, b=-1) == PKV_ERR_SHAPE
+    assert write_decode(L, nb=2**31 // 16) == PKV_ERR_SHAPE
+    for name in ("out", "q", "k", "v", "key", "value", "slots", "bt", "ctx"):
+        assert write_decode(L, **{name: None}) == PKV_ERR_NULL, name
+    need = L.paged_attention_decode_workspace_size(2, 8, 128, 64, 16)
+    assert write_decode(L, ws=None) == PKV_ERR_WORKSPACE
+    assert write_decode(L, wsb=need - 1) == PKV_ERR_WORKSPACE
+    assert write_decode(L, b=0, q=None, key=None) == PKV_OK     # empty batch
+
+
 def test_decode_workspace_size(L):
     # one 512-token partition -> no workspace
     assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == 0
