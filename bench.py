@@ -239,6 +239,7 @@ def main():
         evict()
         step()
     torch.cuda.synchronize()
+    clocks0 = gpu_clocks()
     tm = Timer(torch, args.steps)
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -378,6 +379,24 @@ def main():
                              "partition_tokens": binding.decode_partition_tokens(
                                  m.num_seqs, m.num_q_heads, m.num_kv_heads,
                                  m.max_blocks_per_seq, m.block_size, tdt(m.dtype))}
+            if c == 3:
+                # the ragged batch's decode step too (write + attention): one
+                # fused call, and the two calls
+                nk = torch.randn(m.num_seqs, m.num_kv_heads, m.head_dim, dtype=tdt(m.dtype),
+                                 device=dev)
+                nv = torch.randn_like(nk)
+                ns = ints(m.slot_mapping[m.new_token_rows])
+                ms, _ = time_calls(lambda: binding.paged_kv_write_decode(
+                    tt["out"], tt["q"], tt["k"], tt["v"], nk, nv, ns, tt["bt"], tt["ctx"],
+                    m.block_size, m.scale, workspace=tt["ws"]), n_extra)
+
+                def two_calls():
+                    binding.paged_kv_write(tt["k"], tt["v"], nk, nv, ns)
+                    run_decode(m, tt)
+                ms2, _ = time_calls(two_calls, n_extra)
+                extra[m.name]["step_us"] = round(statistics.mean(ms) * 1e3, 2)
+                extra[m.name]["two_call_step_us"] = round(statistics.mean(ms2) * 1e3, 2)
+                del nk, nv
             del tt
             torch.cuda.empty_cache()
         # int8 cache on the LLaMA-7B shape: the same decode over 1-byte codes
@@ -542,10 +561,29 @@ def main():
         torch.cuda.empty_cache()
         result["other_workloads"] = extra
 
+    result["gpu_clocks"] = {"before": clocks0, "after": gpu_clocks()}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
 
     print(json.dumps(result), flush=True)
+
+
+def gpu_clocks():
+    """Current shader and memory clock levels of the GPU (the DPM level the
+    driver marks active in sysfs), or None where sysfs does not show them."""
+    import glob
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(card, name)) as f:
+                    cur = [ln.split(":", 1)[1].strip().rstrip("*").strip()
+                           for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out.setdefault(os.path.basename(os.path.dirname(card)), {})[name[3:]] = cur[0]
+    return out or None
 
 
 def cpu_baseline():
@@ -583,13 +621,57 @@ def cpu_baseline():
         if dt >= 10.0 or steps >= 200:
             break
     kv_bytes = steps * sum(int(case.seq_lens[b]) for b, _ in pairs) * 2 * case.head_dim * 2
+    per_config = oracle_per_config()
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
             "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full decode steps of the LLaMA-7B-shaped batch, each an oracle "
                       f"KV write of the 8 new tokens then all {len(pairs)} (sequence, head) pairs "
                       f"over 2048 tokens; {dt:.2f} s",
             "us_per_step": round(dt / steps * 1e6, 1),
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "per_config_seconds": per_config}
+
+
+def oracle_per_config():
+    """Wall time of one oracle call per workload (write + attention), on the
+    same host threads: tiny decode, ragged GQA decode and packed prefill in
+    full; the long-context decode from a sample of (sequence, head) pairs of
+    one 131072-token bf16 context, scaled to its 4 x 64 pairs."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_39_amd import workloads as wl
+
+    res = {}
+    for c, key in ((1, "tiny_decode"), (3, "ragged_gqa_decode")):
+        case = wl.workload(c)
+        t0 = time.perf_counter()
+        k, v = oracle.write_kv(case.empty_pool(), case.empty_pool(), case.key, case.value,
+                               case.slot_mapping, case.block_size)
+        oracle.decode(case.q, k, v, case.block_table, case.seq_lens, case.block_size,
+                      case.scale, case.dtype)
+        res[key] = round(time.perf_counter() - t0, 3)
+    case = wl.workload(4)
+    t0 = time.perf_counter()
+    k, v = oracle.write_kv(case.empty_pool(), case.empty_pool(), case.key, case.value,
+                           case.slot_mapping, case.block_size)
+    oracle.varlen(case.q, case.cu_seqlens_q, k, v, case.block_table, case.seq_lens, True,
+                  case.block_size, case.dtype)
+    res["packed_varlen_prefill"] = round(time.perf_counter() - t0, 3)
+    # one sequence of the long-context shape, one kv head: 2 of its 8 query heads
+    lc = wl.decode_case(1005, [131072], 8, 1, 128, 128, "bf16", spare=0.0)
+    k, v = oracle.write_kv(lc.empty_pool(), lc.empty_pool(), lc.key, lc.value,
+                           lc.slot_mapping, lc.block_size)
+    t0 = time.perf_counter()
+    oracle.decode(lc.q, k, v, lc.block_table, lc.seq_lens, lc.block_size, lc.scale, "bf16",
+                  pairs=[(0, 0), (0, 1)])
+    per_pair = (time.perf_counter() - t0) / 2
+    res["long_context_decode_estimated"] = round(per_pair * 4 * 64, 3)
+    res["long_context_decode_note"] = "2 (sequence, head) pairs of one 131072-token context " \
+                                      "timed, scaled to the 256 pairs of the call"
+    del k, v
+    return res
 
 
 if __name__ == "__main__":
