@@ -287,17 +287,16 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   // queries and (APP) the new token's row and slot depend only on the
   // workgroup's indices: they are fetched in one round trip.
   const int row_stride = num_kv_heads * D;
-  // APP: 2 x CPR threads of the kv head's first head group hold a 16-byte
-  // chunk of the new K (then V) row; the workgroup of the partition holding
-  // position ctx-1 (partition 0 for an empty context) stores it
-  const bool app_lane = APP && h0 == kvh * group && tid < 2 * CPR;
-  u32x4_t app_row = {0u, 0u, 0u, 0u};
+  // APP: every lane holds chunk lch of the new K and V rows of its kv head.
+  // The tile holding position ctx-1 takes them in place of the pool's row;
+  // in the workgroup of the partition holding ctx-1 (partition 0 for an
+  // empty context) and of the kv head's first head group, wave 0's lanes of
+  // rows 0 and 1 store them into the pool.
+  u32x4_t app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
   if constexpr (APP) {
-    if (app_lane) {
-      const uint8_t* src = static_cast<const uint8_t*>(tid >= CPR ? new_v : new_k);
-      app_row = *reinterpret_cast<const u32x4_t*>(
-          src + ((size_t)b * row_stride + kvh * D + (tid % CPR) * EPC) * EB);
-    }
+    const size_t src = ((size_t)b * row_stride + kvh * D + lch * EPC) * EB;
+    app_k = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_k) + src);
+    app_v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_v) + src);
   }
   const int first_blk = (p * part_tokens) >> log2_bs;
   const int nblk_max = min(part_tokens >> log2_bs, max_blocks_per_seq - first_blk);
@@ -319,10 +318,11 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   auto app_store = [&]() {
     if constexpr (APP) {
       const int pw = ctx > 0 ? (ctx - 1) / part_tokens : 0;
-      if (app_lane && p == pw && app_slot >= 0 && (int64_t)app_slot < (num_blocks << log2_bs)) {
-        uint8_t* dst = tid >= CPR ? app_v_cache : app_k_cache;
+      if (wave == 0 && lrow < 2 && h0 == kvh * group && p == pw && app_slot >= 0 &&
+          (int64_t)app_slot < (num_blocks << log2_bs)) {
+        uint8_t* dst = lrow ? app_v_cache : app_k_cache;
         *reinterpret_cast<u32x4_t*>(
-            dst + ((size_t)app_slot * row_stride + kvh * D + (tid % CPR) * EPC) * EB) = app_row;
+            dst + ((size_t)app_slot * row_stride + kvh * D + lch * EPC) * EB) = lrow ? app_v : app_k;
       }
     }
   };
@@ -390,18 +390,8 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       const int tok = min(tg + lrow, ntok - 1);
       const int blk = max(__builtin_amdgcn_readfirstlane(s_blk[tg >> log2_bs]), 0);
       const size_t off = (((size_t)blk * bs + (tok & (bs - 1))) * row_stride + head_off) * EB;
-      const uint8_t* kp = kbytes + off;
-      const uint8_t* vp = vbytes + off;
-      if constexpr (APP) {
-        // (uniform test first: this load's rows are tg .. tg+RPI-1, clamped)
-        if (app_pos >= tg && app_pos < tg + RPI && tok == app_pos) {
-          const size_t src = ((size_t)b * row_stride + head_off) * EB;
-          kp = static_cast<const uint8_t*>(new_k) + src;
-          vp = static_cast<const uint8_t*>(new_v) + src;
-        }
-      }
-      kr[j] = load16<true>(kp);
-      vr[j] = load16<true>(vp);
+      kr[j] = load16<true>(kbytes + off);
+      vr[j] = load16<true>(vbytes + off);
     }
   };
   auto claim = [&]() {   // wave-uniform
@@ -491,6 +481,20 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   int g = wave;
   if (g < ntiles) fetch(g);
   while (g < ntiles) {
+    if constexpr (APP) {
+      // the tile holding position ctx-1 (uniform test): that row's K/V come
+      // from new_k / new_v, whatever the pool held when it was read
+      if (app_pos >= tb + g * TT && app_pos < tb + (g + 1) * TT) {
+#pragma unroll
+        for (int j = 0; j < LPI; ++j) {
+          const int tok = min(min(tb + g * TT + j * RPI, last_grp) + lrow, ntok - 1);
+          if (tok == app_pos) {
+            kr[j] = app_k;
+            vr[j] = app_v;
+          }
+        }
+      }
+    }
     // park tile g in the wave's LDS tile (later LDS reads of this wave see it)
 #pragma unroll
     for (int j = 0; j < LPI; ++j) {
