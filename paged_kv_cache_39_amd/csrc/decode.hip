@@ -281,23 +281,13 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const int lrow = lane / CPR, lch = lane % CPR;
   const int bs = 1 << log2_bs;
   static_assert(NT >= kMaxPartTokens / 16, "one block id per thread");
+  static_assert(!APP || (!Q8 && !EXT), "the fused write is a form of the plain 16-bit decode");
 
   // The context length, the partition's block ids (every entry a full
   // partition would use; those past the context are never read), the
   // queries and (APP) the new token's row and slot depend only on the
   // workgroup's indices: they are fetched in one round trip.
   const int row_stride = num_kv_heads * D;
-  // APP: every lane holds chunk lch of the new K and V rows of its kv head.
-  // The tile holding position ctx-1 takes them in place of the pool's row;
-  // in the workgroup of the partition holding ctx-1 (partition 0 for an
-  // empty context) and of the kv head's first head group, wave 0's lanes of
-  // rows 0 and 1 store them into the pool.
-  u32x4_t app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
-  if constexpr (APP) {
-    const size_t src = ((size_t)b * row_stride + kvh * D + lch * EPC) * EB;
-    app_k = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_k) + src);
-    app_v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_v) + src);
-  }
   const int first_blk = (p * part_tokens) >> log2_bs;
   const int nblk_max = min(part_tokens >> log2_bs, max_blocks_per_seq - first_blk);
   const int id_raw =
@@ -315,14 +305,30 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
   const int app_slot = APP ? slot_mapping[b] : -1;
   const int part_start = p * part_tokens;
-  auto app_store = [&]() {
+  // APP: the pool row is stored by the workgroup of the partition holding
+  // ctx-1 (partition 0 for an empty context) and of the kv head's first head
+  // group, from its wave 0, lanes of rows 0 (K) and 1 (V), chunk lch each
+  const size_t app_src = ((size_t)b * row_stride + kvh * D + lch * EPC) * EB;
+  const bool app_writer = APP && wave == 0 && h0 == kvh * group &&
+                          p == (ctx > 0 ? (ctx - 1) / part_tokens : 0) && app_slot >= 0 &&
+                          (int64_t)app_slot < (num_blocks << log2_bs);
+  auto app_put = [&](const u32x4_t& kc, const u32x4_t& vc) {
+    if (lrow < 2) {
+      uint8_t* dst = lrow ? app_v_cache : app_k_cache;
+      *reinterpret_cast<u32x4_t*>(
+          dst + ((size_t)app_slot * row_stride + kvh * D + lch * EPC) * EB) = lrow ? vc : kc;
+    }
+  };
+  auto app_load = [&](u32x4_t& kc, u32x4_t& vc) {
+    kc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_k) + app_src);
+    vc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_v) + app_src);
+  };
+  auto app_store = [&]() {   // the store when no tile of the workgroup holds the row
     if constexpr (APP) {
-      const int pw = ctx > 0 ? (ctx - 1) / part_tokens : 0;
-      if (wave == 0 && lrow < 2 && h0 == kvh * group && p == pw && app_slot >= 0 &&
-          (int64_t)app_slot < (num_blocks << log2_bs)) {
-        uint8_t* dst = lrow ? app_v_cache : app_k_cache;
-        *reinterpret_cast<u32x4_t*>(
-            dst + ((size_t)app_slot * row_stride + kvh * D + lch * EPC) * EB) = lrow ? app_v : app_k;
+      if (app_writer) {
+        u32x4_t kc, vc;
+        app_load(kc, vc);
+        app_put(kc, vc);
       }
     }
   };
@@ -344,9 +350,10 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
   const int nblk = (ntok + bs - 1) >> log2_bs;
   if (tid < nblk) s_blk[tid] = (id_raw >= 0 && id_raw < num_blocks) ? id_raw : -1;
-  if (tid == 0) s_claim = WAVES;
+  // APP: wave 0 takes the last tile (the one holding ctx-1) first and the
+  // counter hands out the others, so only that first step differs
+  if (tid == 0) s_claim = APP ? WAVES - 1 : WAVES;
   __syncthreads();
-  app_store();
 
   // local token whose K/V come from new_k / new_v (-1: none)
   int app_pos = -1;
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       const int blk = s_blk[last >> log2_bs];
       if (blk >= 0 && (int64_t)blk * bs + (last & (bs - 1)) == (int64_t)app_slot) app_pos = last;
     }
+    if (app_pos < 0) app_store();   // slot_mapping[b] is not the slot of ctx-1
   }
 
   const int head_off = kvh * D + lch * EPC;
@@ -478,23 +486,44 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
   };
 
+  // claimed tiles run over [0, nclaim); APP keeps the last one for wave 0
+  const int nclaim = APP ? ntiles - 1 : ntiles;
   int g = wave;
-  if (g < ntiles) fetch(g);
-  while (g < ntiles) {
-    if constexpr (APP) {
-      // the tile holding position ctx-1 (uniform test): that row's K/V come
-      // from new_k / new_v, whatever the pool held when it was read
-      if (app_pos >= tb + g * TT && app_pos < tb + (g + 1) * TT) {
+  if constexpr (APP) {
+    g = wave - 1;
+    if (wave == 0 && ntiles > 0) {
+      // the last tile, with the new row's K/V (fetched with it) in place of
+      // the pool's row at ctx-1, whatever the pool held when it was read
+      const int gl = ntiles - 1;
+      u32x4_t app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
+      fetch(gl);
+      if (app_pos >= 0) app_load(app_k, app_v);
+      if (app_pos >= 0) {
 #pragma unroll
         for (int j = 0; j < LPI; ++j) {
-          const int tok = min(min(tb + g * TT + j * RPI, last_grp) + lrow, ntok - 1);
+          const int tok = min(min(tb + gl * TT + j * RPI, last_grp) + lrow, ntok - 1);
           if (tok == app_pos) {
             kr[j] = app_k;
             vr[j] = app_v;
           }
         }
+        if (app_writer) app_put(app_k, app_v);
       }
+#pragma unroll
+      for (int j = 0; j < LPI; ++j) {
+        *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB) = kr[j];
+        *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB) = vr[j];
+      }
+      g = claim();
+      if (g < nclaim) fetch(g);
+      tile(gl);
+    } else if (g < nclaim) {
+      fetch(g);
     }
+  } else {
+    if (g < ntiles) fetch(g);
+  }
+  while (g < nclaim) {
     // park tile g in the wave's LDS tile (later LDS reads of this wave see it)
 #pragma unroll
     for (int j = 0; j < LPI; ++j) {
@@ -514,7 +543,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       }
     }
     const int gn = claim();
-    if (gn < ntiles) fetch(gn);
+    if (gn < nclaim) fetch(gn);
     tile(g);
     g = gn;
   }
