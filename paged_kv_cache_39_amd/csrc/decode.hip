@@ -238,14 +238,15 @@ struct MfLds {
 // decode query, the last token of its context.
 // APP: the decode step's KV write rides along (one launch instead of two).
 // new_k / new_v [B, Hkv, D] hold each sequence's new token, slot_mapping[b]
-// its pool slot (skipped when negative or past the pool). One workgroup per
-// (sequence, kv head) stores the row into the pool; every workgroup whose
-// partition holds the last position ctx-1 takes that token's K/V from
-// new_k / new_v instead of the pool when slot_mapping[b] is the table's slot
-// of ctx-1 -- the values the write stores there -- so no workgroup waits for
-// the store. The result equals the write followed by the decode as long as
-// no other sequence of the call reads that slot (a sequence's last block is
-// its own).
+// its pool slot (skipped when negative or past the pool). In every
+// workgroup whose partition holds the last position ctx-1, wave 0 walks the
+// partition's last tile first and fetches the new row with it; when
+// slot_mapping[b] is the table's slot of ctx-1 that row replaces the pool's
+// (the values the write stores there), so no workgroup waits for the store,
+// and the workgroup of the kv head's first head group stores it into the
+// pool. The result equals the write followed by the decode as long as no
+// other sequence of the call reads that slot (a sequence's last block is its
+// own).
 template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT, bool APP>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
