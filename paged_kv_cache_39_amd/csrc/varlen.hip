@@ -260,7 +260,6 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // a row max exceeds it by more than 2^8 (P then stays <= 256)
   constexpr float kRescale = 8.f;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * L::stageB];
-  __shared__ int s_tile[5];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps derived addresses scalar
@@ -280,10 +279,12 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int bq = kVlRows / group;   // query positions per tile
   const int bs = 1 << log2_bs;
 
-  // Wave 0 locates the tile. Lane s first reads sequence s's metadata
-  // (first row, Lq, Lk) in one round trip; the tile's sequence then takes
-  // its metadata from that lane.
-  if (wave == 0) {
+  // Every wave locates the tile (same inputs, same result: no LDS hand-off
+  // and no barrier). Lane s first reads sequence s's metadata (first row,
+  // Lq, Lk) in one round trip; the tile's sequence then takes its metadata
+  // from that lane.
+  int tl[5];
+  {
     int my_r0 = 0, my_lq = 0, my_lk = 0;
     if (lane < num_seqs) {
       my_r0 = max(0, min(cu_seqlens_q[lane], total_q));
@@ -318,21 +319,18 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       lq_ = max(0, min(cu_seqlens_q[seq + 1], total_q) - r0);
       lk_ = max(0, min(seq_lens[seq], max_blocks_per_seq << log2_bs));
     }
-    if (lane == 0) {
-      s_tile[0] = seq;
-      s_tile[1] = q0;
-      s_tile[2] = r0;
-      s_tile[3] = lq_;
-      s_tile[4] = lk_;
-    }
+    tl[0] = seq;
+    tl[1] = q0;
+    tl[2] = r0;
+    tl[3] = lq_;
+    tl[4] = lk_;
   }
-  barrier_lds_ops();
-  const int b = s_tile[0];
-  if (b < 0) return;
-  const int q0 = s_tile[1];
-  const int row0 = s_tile[2];
-  const int lq = s_tile[3];
-  const int lk = s_tile[4];
+  const int b = __builtin_amdgcn_readfirstlane(tl[0]);
+  if (b < 0) return;   // the same in every wave
+  const int q0 = __builtin_amdgcn_readfirstlane(tl[1]);
+  const int row0 = __builtin_amdgcn_readfirstlane(tl[2]);
+  const int lq = __builtin_amdgcn_readfirstlane(tl[3]);
+  const int lk = __builtin_amdgcn_readfirstlane(tl[4]);
   const int delta = lk - lq;
 
   // rows of this lane: r = wave*32 + mt*16 + l16 -> (query i = r / group, head r % group)
@@ -456,8 +454,6 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
   };
 
-  if (kv_lo < kv_hi) stage(0, kv_lo);
-
   // Q^T operands (B of S^T = K Q^T): lane holds Q[row][32s + 8*g4 .. +8]
   u32x4_t qb[2][KS];
 #pragma unroll
@@ -470,6 +466,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
                       : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+
+  if (kv_lo < kv_hi) stage(0, kv_lo);
 
   // the queries and the first stage are needed before anything else; waiting
   // for both here keeps the compiler from placing a full wait later, when
