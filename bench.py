@@ -573,6 +573,25 @@ def main():
             "hbm_peak_frac": round(cbytes / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": cbytes}
         del kc, vc
         torch.cuda.empty_cache()
+        # the packed prefill's KV write: every token of the 16 sequences
+        # (slot_mapping over the bs-128 pool), 2 KiB rows of K and of V
+        m = wl.workload(4, values=False)
+        kc = torch.empty(m.pool_shape(), dtype=tdt(m.dtype), device=dev)
+        vc = torch.empty_like(kc)
+        ntok = int(m.slot_mapping.shape[0])
+        nkey = torch.randn(ntok, m.num_kv_heads, m.head_dim, dtype=tdt(m.dtype), device=dev)
+        nval = torch.randn_like(nkey)
+        smap = ints(m.slot_mapping)
+        ms, kms = time_calls(lambda: binding.paged_kv_write(kc, vc, nkey, nval, smap), n_extra)
+        mu = statistics.mean(ms)
+        wbytes = 2 * 2 * ntok * m.num_kv_heads * m.head_dim * wl.ELEM_BYTES[m.dtype] + 4 * ntok
+        extra["kv_write_prefill_16seq_bf16"] = {
+            "us": round(mu * 1e3, 2), "gbs": round(wbytes / (mu * 1e-3) / 1e9, 1),
+            "hbm_peak_frac": round(wbytes / (mu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes": wbytes, "tokens": ntok,
+            "kernel_us": round(statistics.mean(kms) * 1e3, 2)}
+        del kc, vc, nkey, nval
+        torch.cuda.empty_cache()
         result["other_workloads"] = extra
 
     result["gpu_clocks"] = {"before": clocks0, "after": gpu_clocks()}
