@@ -431,10 +431,28 @@ def main():
         mu = statistics.mean(ms)
         b8 = m.decode_bytes() - m.kv_bytes_read() // 2
         gbs = b8 / (mu * 1e-3) / 1e9
+        # its decode step (write the 8 new rows as codes + attend): one fused
+        # call, and the two calls
+        nk8 = torch.randn(m.num_seqs, m.num_kv_heads, m.head_dim, dtype=tdt(m.dtype), device=dev)
+        nv8 = torch.randn_like(nk8)
+        ns8 = ints(m.slot_mapping[m.new_token_rows])
+        ms_f, kms_f = time_calls(lambda: binding.paged_kv_write_decode_int8(
+            o8, q8, k8, v8, nk8, nv8, ksd, vsd, ns8, bt8, ctx8, m.block_size, m.scale,
+            workspace=ws8), n_extra)
+
+        def two_calls8():
+            binding.paged_kv_write_int8(k8, v8, nk8, nv8, ksd, vsd, ns8)
+            binding.paged_attention_decode_int8(o8, q8, k8, v8, ksd, vsd, bt8, ctx8,
+                                                m.block_size, m.scale, workspace=ws8)
+        ms_2, _ = time_calls(two_calls8, n_extra)
         extra["int8_kv_decode_llama7b_b8_ctx2048"] = {
             "us": round(mu * 1e3, 2), "gbs": round(gbs, 1),
             "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b8,
-            "kernel_us": round(statistics.mean(kms) * 1e3, 2)}
+            "kernel_us": round(statistics.mean(kms) * 1e3, 2),
+            "step_us": round(statistics.mean(ms_f) * 1e3, 2),
+            "step_kernel_us": round(statistics.mean(kms_f) * 1e3, 2),
+            "two_call_step_us": round(statistics.mean(ms_2) * 1e3, 2)}
+        del nk8, nv8
         del k8, v8
         torch.cuda.empty_cache()
         for c in (4, 6):

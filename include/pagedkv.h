@@ -332,6 +332,25 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_kv_write_decode_int8 -- one decode step over an int8 cache in a
+ * single launch: paged_kv_write_int8(k_cache, v_cache, key, value, k_scale,
+ * v_scale, slot_mapping, num_seqs tokens) followed by
+ * paged_attention_decode_int8(...) on the same arguments, as
+ * paged_kv_write_decode composes the 16-bit calls. key/value [num_seqs, num_kv_heads,
+ * head_dim] are of dtype (fp16 or bf16, the q dtype); the codes stored and
+ * attended are those paged_kv_write_int8 computes. Same precondition and
+ * workspace rule as paged_kv_write_decode.
+ */
+int paged_kv_write_decode_int8(void* out, const void* q, void* k_cache, void* v_cache,
+                               const void* key, const void* value, const float* k_scale,
+                               const float* v_scale, const int32_t* slot_mapping,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t block_size, float scale, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_copy_blocks -- copy whole cache blocks: for every pair i,
  * block pairs[2i+1] of k_cache and of v_cache becomes a copy of block
  * pairs[2i] (all block_size rows, all kv heads, all dims; bit copy). This is

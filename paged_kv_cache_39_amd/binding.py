@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_float, i32, i32, i32, i32, i32, i64, i32,
                                             vp, sz, vp]
         L.paged_kv_write_decode.restype = ctypes.c_int
+        L.paged_kv_write_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 i32, ctypes.c_float, i32, i32, i32, i32, i32,
+                                                 i64, i32, vp, sz, vp]
+        L.paged_kv_write_decode_int8.restype = ctypes.c_int
         L.paged_attention_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i64,
                                              i32, i32, i32, i32, i32, i64, i32, vp]
         L.paged_attention_varlen.restype = ctypes.c_int
@@ -561,6 +565,45 @@ class BlockManager:
         if got < 0:
             raise PagedKVError("pkv_bm_take_copies", int(got), status_string(int(got)))
         return out[:got]
+
+
+def paged_kv_write_decode_int8(out, q, k_cache, v_cache, key, value, k_scale, v_scale,
+                               slot_mapping, block_table, context_lens, block_size, scale,
+                               workspace=None, stream=None):
+    """One decode step over an int8 cache in one launch: key[b] / value[b]
+    (q's dtype) are quantised with the kv head's scales and stored at pool row
+    slot_mapping[b], then out [B, Hq, D] attends over context_lens[b] tokens."""
+    nb, bs, hkv, d = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    for n, t in (("out", out), ("q", q), ("key", key), ("value", value)):
+        _need_gpu(n, t)
+    for n, t in (("slot_mapping", slot_mapping), ("block_table", block_table),
+                 ("context_lens", context_lens)):
+        _need_gpu(n, t, torch.int32)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [num_seqs, Hq, D]")
+    for t in (out, key, value):
+        if t.dtype != q.dtype:
+            raise TypeError("out/key/value must have q's dtype")
+    bsz, hq, _ = q.shape
+    if key.shape != (bsz, hkv, d) or value.shape != key.shape or slot_mapping.shape != (bsz,):
+        raise ValueError("key/value must be [num_seqs, Hkv, D], slot_mapping [num_seqs]")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    maxblk = block_table.shape[1]
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    need = paged_attention_decode_workspace_size(bsz, hq, d, maxblk, bs) if bsz else 0
+    if workspace is None:
+        workspace = _workspace(need, q.device, s) if need else None
+    elif need:
+        _need_gpu("workspace", workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_kv_write_decode_int8", lib().paged_kv_write_decode_int8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_table), _ptr(context_lens), bs,
+        float(scale), bsz, hq, hkv, d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes,
+        _stream(s)))
 
 
 def time_next_kernel(start_event, stop_event) -> None:

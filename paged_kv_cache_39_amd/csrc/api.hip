@@ -437,6 +437,60 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_kv_write_decode_int8(void* out, const void* q, void* k_cache, void* v_cache,
+                               const void* key, const void* value, const float* k_scale,
+                               const float* v_scale, const int32_t* slot_mapping,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t block_size, float scale, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_DTYPE;  // matrix-core path
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !key || !value || !k_scale || !v_scale ||
+      !slot_mapping || !block_table || !context_lens)
+    return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                            max_blocks_per_seq, block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.dtype = dtype;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
+                                                                          block_size);
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.app_k_cache = k_cache;
+  a.app_v_cache = v_cache;
+  a.new_key = key;
+  a.new_value = value;
+  a.slot_mapping = slot_mapping;
+  hipError_t err = pkv::launch_write_decode_int8(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t num_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int64_t num_blocks, int32_t dtype, void* stream) {

@@ -246,7 +246,8 @@ struct MfLds {
 // and the workgroup of the kv head's first head group stores it into the
 // pool. The result equals the write followed by the decode as long as no
 // other sequence of the call reads that slot (a sequence's last block is its
-// own).
+// own). Over an int8 cache (Q8) the new row is quantised with the kv head's
+// scales first, to the codes the int8 write would store.
 template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT, bool APP>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   const int lrow = lane / CPR, lch = lane % CPR;
   const int bs = 1 << log2_bs;
   static_assert(NT >= kMaxPartTokens / 16, "one block id per thread");
-  static_assert(!APP || (!Q8 && !EXT), "the fused write is a form of the plain 16-bit decode");
+  static_assert(!APP || !EXT, "the fused write is a form of the plain decode");
 
   // The context length, the partition's block ids (every entry a full
   // partition would use; those past the context are never read), the
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   // APP: the pool row is stored by the workgroup of the partition holding
   // ctx-1 (partition 0 for an empty context) and of the kv head's first head
   // group, from its wave 0, lanes of rows 0 (K) and 1 (V), chunk lch each
-  const size_t app_src = ((size_t)b * row_stride + kvh * D + lch * EPC) * EB;
+  // element index of the lane's chunk of the new row (new_k / new_v hold Ty)
+  const size_t app_src = (size_t)b * row_stride + kvh * D + lch * EPC;
   const bool app_writer = APP && wave == 0 && h0 == kvh * group &&
                           p == (ctx > 0 ? (ctx - 1) / part_tokens : 0) && app_slot >= 0 &&
                           (int64_t)app_slot < (num_blocks << log2_bs);
@@ -320,9 +322,20 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
           dst + ((size_t)app_slot * row_stride + kvh * D + lch * EPC) * EB) = lrow ? vc : kc;
     }
   };
+  // the lane's chunk of the new K / V row in the cache's form: the 16-bit
+  // values, or (int8 cache) their 16 codes under the kv head's scales, the
+  // same codes the int8 write stores
   auto app_load = [&](u32x4_t& kc, u32x4_t& vc) {
-    kc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_k) + app_src);
-    vc = *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(new_v) + app_src);
+    using S = typename Ty::storage;
+    if constexpr (Q8) {
+      const uint4 kq = quantize16<Ty>(static_cast<const S*>(new_k) + app_src, k_scale[kvh]);
+      const uint4 vq = quantize16<Ty>(static_cast<const S*>(new_v) + app_src, v_scale[kvh]);
+      kc = u32x4_t{kq.x, kq.y, kq.z, kq.w};
+      vc = u32x4_t{vq.x, vq.y, vq.z, vq.w};
+    } else {
+      kc = *reinterpret_cast<const u32x4_t*>(static_cast<const S*>(new_k) + app_src);
+      vc = *reinterpret_cast<const u32x4_t*>(static_cast<const S*>(new_v) + app_src);
+    }
   };
   auto app_store = [&]() {   // the store when no tile of the workgroup holds the row
     if constexpr (APP) {
@@ -487,6 +500,28 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
   };
 
+  // park the fetched tile in the wave's LDS tile (int8 codes widened on the
+  // way); later LDS reads of this wave see it
+  auto park = [&]() {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) {
+      uint8_t* dk = s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+      uint8_t* dv = s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
+      if constexpr (Q8) {
+        u32x4_t lo, hi;
+        widen_i8x16<Ty>(kr[j], lo, hi);
+        *reinterpret_cast<u32x4_t*>(dk) = lo;
+        *reinterpret_cast<u32x4_t*>(dk + 16) = hi;
+        widen_i8x16<Ty>(vr[j], lo, hi);
+        *reinterpret_cast<u32x4_t*>(dv) = lo;
+        *reinterpret_cast<u32x4_t*>(dv + 16) = hi;
+      } else {
+        *reinterpret_cast<u32x4_t*>(dk) = kr[j];
+        *reinterpret_cast<u32x4_t*>(dv) = vr[j];
+      }
+    }
+  };
+
   // claimed tiles run over [0, nclaim); APP keeps the last one for wave 0
   const int nclaim = APP ? ntiles - 1 : ntiles;
   int g = wave;
@@ -510,11 +545,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
         }
         if (app_writer) app_put(app_k, app_v);
       }
-#pragma unroll
-      for (int j = 0; j < LPI; ++j) {
-        *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB) = kr[j];
-        *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB) = vr[j];
-      }
+      park();
       g = claim();
       if (g < nclaim) fetch(g);
       tile(gl);
@@ -525,24 +556,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     if (g < ntiles) fetch(g);
   }
   while (g < nclaim) {
-    // park tile g in the wave's LDS tile (later LDS reads of this wave see it)
-#pragma unroll
-    for (int j = 0; j < LPI; ++j) {
-      uint8_t* dk = s_k + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
-      uint8_t* dv = s_v + (j * RPI + lrow) * L::rowB + lch * 32 / EB;
-      if constexpr (Q8) {
-        u32x4_t lo, hi;
-        widen_i8x16<Ty>(kr[j], lo, hi);
-        *reinterpret_cast<u32x4_t*>(dk) = lo;
-        *reinterpret_cast<u32x4_t*>(dk + 16) = hi;
-        widen_i8x16<Ty>(vr[j], lo, hi);
-        *reinterpret_cast<u32x4_t*>(dv) = lo;
-        *reinterpret_cast<u32x4_t*>(dv + 16) = hi;
-      } else {
-        *reinterpret_cast<u32x4_t*>(dk) = kr[j];
-        *reinterpret_cast<u32x4_t*>(dv) = vr[j];
-      }
-    }
+    park();
     const int gn = claim();
     if (gn < nclaim) fetch(gn);
     tile(g);
@@ -766,6 +780,15 @@ hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {
                : launch_decode_mfma<F16, 128, true>(a, stream);
   return d64 ? launch_decode_mfma<BF16, 64, true>(a, stream)
              : launch_decode_mfma<BF16, 128, true>(a, stream);
+}
+
+hipError_t launch_write_decode_int8(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_dim == 64;
+  if (a.dtype == 1)
+    return d64 ? launch_decode_mfma<F16, 64, true, false, true>(a, stream)
+               : launch_decode_mfma<F16, 128, true, false, true>(a, stream);
+  return d64 ? launch_decode_mfma<BF16, 64, true, false, true>(a, stream)
+             : launch_decode_mfma<BF16, 128, true, false, true>(a, stream);
 }
 
 hipError_t launch_write_decode(const DecodeArgs& a, hipStream_t stream) {

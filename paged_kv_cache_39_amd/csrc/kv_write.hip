@@ -94,25 +94,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
 // 16-byte store into the pool.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s) {
-  auto q = [s](float x) -> uint32_t {
-    const float r = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.f), 127.f);
-    return (uint32_t)(int32_t)r & 0xFFu;
-  };
-  return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
-}
-
-template <class Ty>
-__device__ __forceinline__ uint4 quantize16(const typename Ty::storage* x, float s) {
-  const Chunk<Ty, 16> c = load_chunk<Ty, 16>(x);
-  uint4 r;
-  r.x = quantize4(c.get(0), c.get(1), c.get(2), c.get(3), s);
-  r.y = quantize4(c.get(4), c.get(5), c.get(6), c.get(7), s);
-  r.z = quantize4(c.get(8), c.get(9), c.get(10), c.get(11), s);
-  r.w = quantize4(c.get(12), c.get(13), c.get(14), c.get(15), s);
-  return r;
-}
-
 template <class Ty>
 __global__ __launch_bounds__(256) void kv_write_int8_kernel(
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,

@@ -289,6 +289,28 @@ __device__ __forceinline__ void widen_i8x16(const u32x4_t c, u32x4_t& lo, u32x4_
   hi = u32x4_t{r[4], r[5], r[6], r[7]};
 }
 
+// int8 code of x under a per-kv-head scale s: clamp(rne(x / s), -127, 127),
+// the quotient an IEEE binary32 division. quantize16: 16 consecutive
+// elements of a row -> 16 codes (byte k = code k).
+__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s) {
+  auto q = [s](float x) -> uint32_t {
+    const float r = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.f), 127.f);
+    return (uint32_t)(int32_t)r & 0xFFu;
+  };
+  return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
+}
+
+template <class Ty>
+__device__ __forceinline__ uint4 quantize16(const typename Ty::storage* x, float s) {
+  const Chunk<Ty, 16> c = load_chunk<Ty, 16>(x);
+  uint4 r;
+  r.x = quantize4(c.get(0), c.get(1), c.get(2), c.get(3), s);
+  r.y = quantize4(c.get(4), c.get(5), c.get(6), c.get(7), s);
+  r.z = quantize4(c.get(8), c.get(9), c.get(10), c.get(11), s);
+  r.w = quantize4(c.get(12), c.get(13), c.get(14), c.get(15), s);
+  return r;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane i supplies the address of a row R_i of four 16-bit elements; lane
 // 4a+b receives (R_a[b], R_{a+4}[b], R_{a+8}[b], R_{a+12}[b]).

@@ -120,6 +120,9 @@ hipError_t launch_decode_ext(const DecodeArgs& a, hipStream_t stream);
 // the decode step's KV write (one new token per sequence) and the decode in
 // one launch (fp16 / bf16; an fp32 pool takes the two kernels in turn)
 hipError_t launch_write_decode(const DecodeArgs& a, hipStream_t stream);
+// the same over an int8 cache: the new rows are quantised with the kv head's
+// scales (as the int8 write does), stored and attended in one launch
+hipError_t launch_write_decode_int8(const DecodeArgs& a, hipStream_t stream);
 // int8 cache (codes), q/out of a.dtype (fp16 or bf16)
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
 

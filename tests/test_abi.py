@@ -126,6 +126,27 @@ def test_write_decode_validation(L):
     assert write_decode(L, b=0, q=None, key=None) == PKV_OK     # empty batch
 
 
+def test_write_decode_int8_validation(L):
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, key=FAKE, value=FAKE, ks=FAKE, vs=FAKE,
+                 slots=FAKE, bt=FAKE, ctx=FAKE, bs=16, scale=0.1, b=2, hq=8, hkv=2, d=128,
+                 maxblk=64, nb=256, dtype=1, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.paged_kv_write_decode_int8(a["out"], a["q"], a["k"], a["v"], a["key"],
+                                            a["value"], a["ks"], a["vs"], a["slots"], a["bt"],
+                                            a["ctx"], a["bs"], a["scale"], a["b"], a["hq"],
+                                            a["hkv"], a["d"], a["maxblk"], a["nb"], a["dtype"],
+                                            a["ws"], a["wsb"], None)
+    assert call(dtype=0) == PKV_ERR_DTYPE          # q must be fp16 / bf16
+    assert call(dtype=3) == PKV_ERR_DTYPE
+    assert call(hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert call(d=80) == PKV_ERR_UNSUPPORTED
+    for name in ("out", "q", "k", "v", "key", "value", "ks", "vs", "slots", "bt", "ctx"):
+        assert call(**{name: None}) == PKV_ERR_NULL, name
+    assert call(ws=None) == PKV_ERR_WORKSPACE
+    assert call(b=0, q=None) == PKV_OK
+
+
 def test_decode_workspace_size(L):
     # one 512-token partition -> no workspace
     assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == 0

@@ -145,3 +145,98 @@ def test_int8_decode_4096_partitions():
     rng = np.random.default_rng(3)
     pairs = sorted({(b, int(h)) for b in range(len(lens)) for h in rng.choice(32, size=4, replace=False)})
     check_decode(Int8Case(case), pairs=pairs)
+
+
+# ---------------------------------------------------------------------------
+# the decode step in one call over the int8 cache (paged_kv_write_decode_int8):
+# all but each sequence's last token are written first (the other cells keep
+# the sentinel); the call must store the oracle's codes of the new rows and
+# attend as the oracle's decode over the codes after that write
+# ---------------------------------------------------------------------------
+
+def check_write_decode_int8(case, pairs=None, seed=0):
+    print(f"int8 write+decode parity: {case.name} dtype={case.dtype} "
+          f"ctx={case.seq_lens.tolist()[:8]} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+          f"D={case.head_dim} bs={case.block_size}", flush=True)
+    rng = np.random.default_rng(seed)
+    B, hkv, d = case.num_seqs, case.num_kv_heads, case.head_dim
+    ks, vs = wl.int8_scales(hkv)
+    shape = case.pool_shape()
+    k8 = torch.full(shape, SENTINEL, dtype=torch.int8, device="cuda")
+    v8 = torch.full(shape, SENTINEL, dtype=torch.int8, device="cuda")
+    ksd, vsd = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    slots = case.slot_mapping.copy()
+    used = set(int(x) for x in case.block_table.ravel() if x >= 0)
+    spare = [blk * case.block_size for blk in range(case.num_blocks) if blk not in used]
+    pre = slots.copy()
+    nk = np.zeros((B, hkv, d), dtype=case.key.dtype)
+    nv = np.zeros_like(nk)
+    sm = np.full(B, -1, np.int32)
+    extra = []
+    rows = iter(case.new_token_rows)
+    for b in range(B):
+        if case.seq_lens[b] > 0:
+            r = int(next(rows))
+            nk[b], nv[b], sm[b] = case.key[r], case.value[r], slots[r]
+            pre[r] = -1
+        else:   # an empty context still stores its row (to a slot no table reads)
+            nk[b] = wl.normal(rng, (hkv, d), case.dtype)
+            nv[b] = wl.normal(rng, (hkv, d), case.dtype)
+            sm[b] = spare.pop()
+            extra.append(b)
+    binding.paged_kv_write_int8(k8, v8, to_device(case.key, case.dtype),
+                                to_device(case.value, case.dtype), ksd, vsd, ints(pre))
+    q = to_device(case.q, case.dtype)
+    out = torch.full_like(q, float("nan"))
+    binding.paged_kv_write_decode_int8(out, q, k8, v8, to_device(nk, case.dtype),
+                                       to_device(nv, case.dtype), ksd, vsd, ints(sm),
+                                       ints(case.block_table), ints(case.seq_lens),
+                                       case.block_size, case.scale)
+    torch.cuda.synchronize()
+    pool = np.full(shape, SENTINEL, np.int8)
+    kh, vh = oracle.write_kv_int8(pool, pool, case.key, case.value, ks, vs, slots,
+                                  case.block_size, case.dtype)
+    if extra:
+        kh, vh = oracle.write_kv_int8(kh, vh, nk[extra], nv[extra], ks, vs, sm[extra],
+                                      case.block_size, case.dtype)
+    assert np.array_equal(k8.cpu().numpy(), kh), "k codes differ from the oracle"
+    assert np.array_equal(v8.cpu().numpy(), vh), "v codes differ from the oracle"
+    want = oracle.decode_int8(case.q, kh, vh, ks, vs, case.block_table, case.seq_lens,
+                              case.block_size, case.scale, case.dtype, pairs=pairs)
+    mask = None
+    if pairs is not None:
+        mask = np.zeros(want.shape, dtype=bool)
+        for b, h in pairs:
+            mask[b, h] = True
+    err = max_abs_err(to_host(out, case.dtype), want, case.dtype, mask)
+    assert err <= ATOL[case.dtype], f"max abs err {err} > {ATOL[case.dtype]}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d,hq,hkv,bs", [(64, 4, 4, 16), (128, 8, 2, 32), (128, 16, 2, 64)])
+def test_int8_write_decode_sweep(dtype, d, hq, hkv, bs):
+    case = wl.decode_case(680 + d + hq + bs, EDGE_LENS, hq, hkv, d, bs, dtype, spare=0.5)
+    check_write_decode_int8(case)
+
+
+def test_int8_write_decode_whole_context_plan():
+    lens = [0, 1, 31, 32, 33, 255, 256, 257, 1023, 1024, 2047, 2048, 1500, 700, 9, 64]
+    case = wl.decode_case(690, lens, 32, 16, 128, 16, "f16", spare=0.2)
+    check_write_decode_int8(case)
+
+
+def test_int8_write_decode_llama7b_shape():
+    """The LLaMA-7B-shaped step (8 x 2048, 32/32 heads, fp16 q): codes
+    everywhere, the output on sampled (sequence, head) pairs."""
+    case = wl.workload(2)
+    rng = np.random.default_rng(2)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 8, 10), rng.integers(0, 32, 10))]
+    check_write_decode_int8(case, pairs=pairs + [(7, 31)])
+
+
+def test_int8_write_decode_long_partitions():
+    case = wl.decode_case(691, [16384, 16383, 4097, 4096, 8191, 1, 0, 12288], 32, 32, 128, 16,
+                          "bf16", spare=0.05)
+    rng = np.random.default_rng(3)
+    pairs = sorted({(b, int(h)) for b in range(8) for h in rng.choice(32, 3, replace=False)})
+    check_write_decode_int8(case, pairs=pairs)
