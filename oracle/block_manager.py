@@ -5,8 +5,7 @@ TEST INFRASTRUCTURE, like the rest of ``oracle/``: only the tests, the smoke
 check and the benchmark's CPU-baseline leg may use it; the library never
 imports it.
 
-What the pages describe, and the readings taken where they are silent (each
-listed in DESIGN.md):
+What the pages describe, and the readings taken where they are silent:
 
 * A pool of ``num_blocks`` fixed-size blocks is allocated once; sequences
   take blocks from a free list as they grow (vLLM-on-CANN page, its

@@ -8,8 +8,7 @@ The pages name int8 KV-cache quantisation as a way to shrink the cache (the
 ``antiquant_mode`` / ``antiquant_scale`` on one API and
 ``dequant_scale_key`` / ``dequant_scale_value`` on the other; its list of
 further KV-cache techniques: "INT8 / W8A8C8" cache quantisation). They fix
-neither the granularity nor the rounding. Readings taken (listed in
-the design doc): symmetric codes with one float32 scale per kv head and per
+neither the granularity nor the rounding. Readings taken: symmetric codes with one float32 scale per kv head and per
 tensor (K and V have their own), value = code * scale; a stored code is
 ``clamp(rne(x / scale), -127, 127)`` with the division done in float32 (the
 precision the kernel takes the same decision in) and rounding half to even.

@@ -29,7 +29,7 @@ What it computes, and where the pages define it:
   output) triples into the softmax over the union (the vLLM-on-CANN page:
   scattered blocks force block-by-block online merging).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 GQA maps query head h to kv head h // (Hq // Hkv); causal alignment is
 bottom-right (query i of a sequence with Lq queries and Lk keys sees keys
 j <= i + Lk - Lq); a query with no allowed key outputs exactly 0; a context

@@ -6,8 +6,7 @@ TEST INFRASTRUCTURE, like the rest of ``oracle/``.
 The skill page lists a "Band" (sliding-window) mask mode for prefill and
 decode that needs a count of preceding tokens (``pre_tokens``), and the FA
 call on the cann-recipes-infer page takes ``alibi_slopes`` for ALiBi
-positional encoding. Neither is spelled out; the readings taken (listed in
-DESIGN.md):
+positional encoding. Neither is spelled out; the readings taken:
 
 * positions are aligned to the last key, as for the causal mask: local query
   i of a sequence with Lq queries and Lk keys sits at p = i + Lk - Lq (a
