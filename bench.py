@@ -130,8 +130,8 @@ class KernelEvents:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are "
-                                   "not part of this build (use --gpus 1)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no "
+                                   "multi-GPU path (use --gpus 1)"}))
         sys.exit(2)
 
     import numpy as np
