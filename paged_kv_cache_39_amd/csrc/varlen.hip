@@ -504,12 +504,12 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   for (int kv0 = kv_lo; kv0 < kv_hi; kv0 += kVlBN, ++it) {
     const int cur = it & 1;
     const bool more = kv0 + kVlBN < kv_hi;
-    if (more) stage(cur ^ 1, kv0 + kVlBN);
-    // this tile's copies (issued one iteration earlier) have landed in LDS;
-    // the next tile's stay in flight
-    if (more) wait_vmcnt<2 * LPT>();
-    else wait_vmcnt<0>();
+    // this tile's copies (issued one iteration earlier) have landed in LDS,
+    // and every wave is past the previous iteration, so the other stage,
+    // read there, may be refilled: one barrier per tile
+    wait_vmcnt<0>();
     barrier_lds_ops();
+    if (more) stage(cur ^ 1, kv0 + kVlBN);
     const uint8_t* sk = s_kv + cur * L::stageB;
     const uint8_t* sv = sk + L::tileB;
     const bool need_mask = kv0 + kVlBN > nomask_end || (windowed && kv0 < mask_lo_end);
@@ -652,7 +652,6 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         }
       }
     }
-    barrier_lds_ops();   // every wave is done with this stage before it is refilled
   }
 
   if (SPLIT && n_chunks > 1) {
