@@ -128,16 +128,23 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
 // causal mask, else Lk. That bound grows with the tile's position, so the
 // tiles of a sequence needing at least w key tiles form a suffix; this
 // returns its length (lq, lk: the sequence's query and key counts).
-__device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, int causal) {
+// x / bq for x >= 0: a shift when bq is a power of two (bq_log2 >= 0, the
+// usual group sizes), else a division
+__device__ __forceinline__ int div_bq(int x, int bq, int bq_log2) {
+  return bq_log2 >= 0 ? (x >> bq_log2) : x / bq;
+}
+
+__device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, int bq_log2,
+                                               int causal) {
   if (lq <= 0) return 0;
-  const int nt = (lq + bq - 1) / bq;
+  const int nt = div_bq(lq + bq - 1, bq, bq_log2);
   if (w <= 0) return nt;
   const int kmin = (w - 1) * kVlBN;   // the loop end must exceed this
   if (lk <= kmin) return 0;
   if (!causal) return nt;
   const int x = kmin - (lk - lq);      // needs min((t + 1) * bq, lq) > x
   if (lq <= x) return 0;
-  return x < 0 ? nt : nt - x / bq;
+  return x < 0 ? nt : nt - div_bq(x, bq, bq_log2);
 }
 
 // Locate query tile `g` of one kv head in longest-first order: tiles sorted
@@ -150,8 +157,8 @@ __device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, in
 __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
                                               const int32_t* __restrict__ seq_lens,
                                               int num_seqs, int total_q, int max_lk, int bq,
-                                              int causal, int g, int lane, int my_lq, int my_lk,
-                                              int& seq, int& q0) {
+                                              int bq_log2, int causal, int g, int lane, int my_lq,
+                                              int my_lk, int& seq, int& q0) {
   auto meta = [&](int s0, int& lq, int& lk) {
     if (s0 == 0) {
       lq = my_lq;
@@ -172,7 +179,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
       int lq, lk;
       meta(s0, lq, lk);
-      c += tiles_with_work(w, lq, lk, bq, causal);
+      c += tiles_with_work(w, lq, lk, bq, bq_log2, causal);
     }
     return wave_sum(c);
   };
@@ -195,8 +202,8 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
     int lq, lk;
     meta(s0, lq, lk);
-    const int ge = tiles_with_work(lo, lq, lk, bq, causal);
-    const int c = ge - tiles_with_work(lo + 1, lq, lk, bq, causal);
+    const int ge = tiles_with_work(lo, lq, lk, bq, bq_log2, causal);
+    const int c = ge - tiles_with_work(lo + 1, lq, lk, bq, bq_log2, causal);
     int incl = c;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -207,7 +214,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     if (r < total) {
       const unsigned long long hit = __ballot(incl - c <= r && r < incl);
       const int L = __builtin_ctzll(hit);
-      const int nt = (__shfl(lq, L, kWave) + bq - 1) / bq;
+      const int nt = div_bq(__shfl(lq, L, kWave) + bq - 1, bq, bq_log2);
       const int t = nt - __shfl(ge, L, kWave) + (r - __shfl(incl - c, L, kWave));
       seq = s0 + L;
       q0 = t * bq;
@@ -277,6 +284,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int xseq = extra ? (slot - n_tiles) / (max_splits - 1) : 0;
   const int group = num_q_heads / num_kv_heads;
   const int bq = kVlRows / group;   // query positions per tile
+  const int bq_log2 = (bq & (bq - 1)) == 0 ? __builtin_ctz(bq) : -1;
   const int bs = 1 << log2_bs;
 
   // Every wave locates the tile (same inputs, same result: no LDS hand-off
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       my_lq = max(0, min(cu_seqlens_q[lane + 1], total_q) - my_r0);
       my_lk = max(0, min(seq_lens[lane], max_blocks_per_seq << log2_bs));
     }
-    const int nt0 = my_lq > 0 ? (my_lq + bq - 1) / bq : 0;
+    const int nt0 = my_lq > 0 ? div_bq(my_lq + bq - 1, bq, bq_log2) : 0;
     int seq = -1, q0 = 0, r0 = 0, lq_ = 0, lk_ = 0;
     // longest-first order; under a window a tile's key count is not
     // monotone in its position, so those tiles go by rank from the end
@@ -306,8 +314,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       found = (EXT && window_left >= 0)
                   ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
                   : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
-                                  max_blocks_per_seq << log2_bs, bq, causal, tile, lane, my_lq,
-                                  my_lk, seq, q0);
+                                  max_blocks_per_seq << log2_bs, bq, bq_log2, causal, tile, lane,
+                                  my_lq, my_lk, seq, q0);
     }
     if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
