@@ -95,7 +95,10 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
  * paged_attention_decode_workspace_size -- bytes of device workspace that
  * paged_attention_decode needs for these sizes: the split-KV partial results,
  * one (max, sum, unnormalised output) triple per sequence, query head and
- * 512-token context partition, fp32. Returns 0 when no workspace is needed
+ * context partition, fp32. Partitions are counted at 512 tokens, or at 128
+ * tokens for small problems (num_seqs x num_q_heads x ceil(max_blocks_per_seq
+ * x block_size / 512) < 4096), where the call may split contexts finer to
+ * give every compute unit work. Returns 0 when no workspace is needed
  * (contexts of at most one partition) and for invalid sizes.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,

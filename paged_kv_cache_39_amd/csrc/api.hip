@@ -38,9 +38,12 @@ int check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64
   return PKV_OK;
 }
 
-int decode_num_parts(int32_t max_blocks_per_seq, int32_t block_size) {
-  // the finest split any launch plan uses
-  return pkv::decode_parts(max_blocks_per_seq, block_size, pkv::kDecodePart);
+int decode_num_parts(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                     int32_t block_size) {
+  // the finest split any launch plan for these sizes uses
+  const bool fine = pkv::decode_fine_ok(num_seqs, num_q_heads, max_blocks_per_seq, block_size);
+  return pkv::decode_parts(max_blocks_per_seq, block_size,
+                           fine ? pkv::kDecodeFinePart : pkv::kDecodePart);
 }
 
 }  // namespace
@@ -137,7 +140,9 @@ int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32
   int hpw = 1;
   for (int c = 16; c >= 1; --c)
     if (group % c == 0) { hpw = c; break; }
-  return pkv::plan_decode(num_seqs, num_q_heads / hpw, max_blocks_per_seq, block_size)
+  return pkv::plan_decode(num_seqs, num_q_heads / hpw, max_blocks_per_seq, block_size,
+                          pkv::decode_fine_ok(num_seqs, num_q_heads, max_blocks_per_seq,
+                                              block_size))
       .part_tokens;
 }
 
@@ -167,7 +172,7 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
                                              int32_t block_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return 0;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return 0;
-  const int64_t parts = decode_num_parts(max_blocks_per_seq, block_size);
+  const int64_t parts = decode_num_parts(num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   if (parts <= 1) return 0;
   const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
   return (size_t)(rows * 2 + rows * head_dim) * sizeof(float);
@@ -209,8 +214,8 @@ int paged_attention_decode(void* out, const void* q, const void* k_cache, const 
   a.num_blocks = num_blocks;
   a.dtype = dtype;
   // partials are laid out for the finest split; a coarser launch plan uses a prefix
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
-                                                                          block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   hipError_t err = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
@@ -255,8 +260,8 @@ int paged_kv_write_decode(void* out, const void* q, void* k_cache, void* v_cache
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
-                                                                          block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   a.app_k_cache = k_cache;
@@ -358,8 +363,8 @@ int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, con
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
-                                                                          block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   a.alibi = alibi_slopes;
@@ -427,8 +432,8 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
-                                                                          block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   a.k_scale = k_scale;
@@ -476,8 +481,8 @@ int paged_kv_write_decode_int8(void* out, const void* q, void* k_cache, void* v_
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(max_blocks_per_seq,
-                                                                          block_size);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
   a.k_scale = k_scale;

@@ -738,7 +738,9 @@ static hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   for (int c = 16; c >= 1; --c)
     if (group % c == 0) { hpw = c; break; }
   const DecodePlan plan = plan_decode(a.num_seqs, a.num_q_heads / hpw, a.max_blocks_per_seq,
-                                      a.block_size);
+                                      a.block_size,
+                                      decode_fine_ok(a.num_seqs, a.num_q_heads,
+                                                     a.max_blocks_per_seq, a.block_size));
   if (plan.waves == 8)
     return launch_mfma_cfg<Ty, D, 8, 32, Q8, EXT, APP>(a, stream, hpw, plan.part_tokens);
   return launch_mfma_cfg<Ty, D, 4, 16, Q8, EXT, APP>(a, stream, hpw, plan.part_tokens);

@@ -53,13 +53,25 @@ inline int decode_parts(int max_blocks_per_seq, int block_size, int part_tokens)
 //   (fewer, longer partitions: fewer workgroup start-ups and a smaller
 //   reduce); when even 1024-token partitions leave the chip short of work,
 //   512-token partitions for 4-wave workgroups.
+// - Small problems (fine_ok): when 512-token partitions still leave CUs
+//   without a workgroup, 256- or 128-token partitions.
 struct DecodePlan {
   int waves;
   int part_tokens;
 };
 constexpr int kDecodeMaxPart = 4096;
 constexpr int kDecodeWgsPerCU = 4;
-inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size) {
+constexpr int kDecodeFinePart = 128;
+// Whether a call may take partitions shorter than 512 tokens: decided from
+// what the workspace-size function is given (no kv head count), and true
+// only for small problems, whose workspace stays small at that granularity.
+inline bool decode_fine_ok(long long num_seqs, long long num_q_heads, int max_blocks_per_seq,
+                           int block_size) {
+  return num_seqs * num_q_heads * decode_parts(max_blocks_per_seq, block_size, kDecodePart) <
+         16LL * kNumCUs;
+}
+inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size,
+                              bool fine_ok) {
   const long long rows = (long long)num_seqs * groups;
   const long long max_ctx = (long long)max_blocks_per_seq * block_size;
   if (rows >= kNumCUs && max_ctx <= kDecodeWidePart) {
@@ -69,7 +81,12 @@ inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, 
   for (int part = kDecodeMaxPart; part >= 2 * kDecodePart; part /= 2)
     if (rows * ((max_ctx + part - 1) / part) >= (long long)kDecodeWgsPerCU * kNumCUs)
       return {8, part};
-  return {4, kDecodePart};
+  int part = kDecodePart;
+  if (fine_ok)
+    while (part > kDecodeFinePart && part > block_size &&
+           rows * ((max_ctx + part - 1) / part) < kNumCUs)
+      part /= 2;
+  return {4, part};
 }
 
 hipError_t launch_kv_write(void* k_cache, void* v_cache, const void* key, const void* value,

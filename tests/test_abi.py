@@ -148,8 +148,12 @@ def test_write_decode_int8_validation(L):
 
 
 def test_decode_workspace_size(L):
-    # one 512-token partition -> no workspace
-    assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == 0
+    # one 512-token partition of a large problem -> no workspace
+    assert L.paged_attention_decode_workspace_size(64, 64, 128, 512 // 16, 16) == 0
+    # a small problem counts 128-token partitions: 8 x 32 x 4 triples
+    assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == \
+        8 * 32 * 4 * (2 + 128) * 4
+    assert L.paged_attention_decode_workspace_size(1, 8, 128, 128 // 16, 16) == 0
     # 131072-token contexts with bs 128: 256 partitions of (max, sum) + D floats
     got = L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128)
     assert got == 4 * 64 * 256 * (2 + 128) * 4
@@ -171,6 +175,11 @@ def test_decode_partition_plan(L):
     assert f(2, 32, 32, 128, 16, 1) == 512
     # fp32 path always splits at 512
     assert f(8, 32, 32, 128, 16, 0) == 512
+    # one sequence with 32/8 heads over 8192 tokens: 512-token partitions give
+    # 8 x 16 = 128 workgroups, fewer than the 256 CUs -> 256-token partitions
+    assert f(1, 32, 8, 512, 16, 2) == 256
+    assert f(1, 32, 8, 256, 16, 2) == 128      # 4096 tokens: 128-token partitions
+    assert f(1, 32, 8, 64, 128, 2) == 256      # 8192 tokens, bs 128: 256 workgroups at 256
     assert f(8, 6, 4, 128, 16, 1) == 0           # invalid head counts
 
 

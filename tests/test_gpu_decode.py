@@ -195,3 +195,20 @@ def test_decode_long_partition_plans(lens, hq, hkv, d, part):
     pairs = sorted({(b, int(h)) for b in range(len(lens))
                     for h in rng.choice(hq, size=4, replace=False)} | {(b, hq - 1) for b in range(len(lens))})
     check_decode(case, pairs=pairs)
+
+
+FINE_PLANS = [
+    ([8192], 32, 8, 16, 256),          # one sequence, 8 kv heads: 128 workgroups at 512 tokens
+    ([4096, 3000], 32, 8, 16, 256),
+    ([8192, 1, 0], 16, 2, 32, 128),
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,bs,part", FINE_PLANS)
+def test_decode_fine_partitions_for_small_problems(lens, hq, hkv, bs, part):
+    """Small problems split contexts below 512 tokens so that every compute
+    unit gets a workgroup; the reduce merges the partitions."""
+    case = wl.decode_case(1600 + part + len(lens), lens, hq, hkv, 128, bs, "bf16")
+    assert binding.decode_partition_tokens(len(lens), hq, hkv, case.max_blocks_per_seq, bs,
+                                           torch.bfloat16) == part
+    check_decode(case)

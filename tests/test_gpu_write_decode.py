@@ -154,3 +154,11 @@ def test_write_decode_llama7b_shape():
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 8, 12), rng.integers(0, 32, 12))]
     pairs += [(0, 0), (7, 31)]
     check_step(case, pairs=pairs)
+
+
+def test_write_decode_fine_partitions():
+    # one sequence with 32/8 heads over 8192 tokens: 256-token partitions
+    case = wl.decode_case(720, [8192], 32, 8, 128, 16, "bf16")
+    assert binding.decode_partition_tokens(1, 32, 8, case.max_blocks_per_seq, 16,
+                                           torch.bfloat16) == 256
+    check_step(case)
