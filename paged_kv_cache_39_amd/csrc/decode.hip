@@ -258,7 +258,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     int64_t num_blocks, int num_parts, int part_tokens, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const float* __restrict__ alibi, int window_left,
     uint8_t* app_k_cache, uint8_t* app_v_cache, const void* __restrict__ new_k,
-    const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping) {
+    const void* __restrict__ new_v, const int32_t* __restrict__ slot_mapping, int xcd_bit) {
   using L = MfLds<D, WAVES, TT>;
   constexpr int NT = WAVES * kWave;
   constexpr int EB = Q8 ? 1 : 2;      // bytes per cached element
@@ -274,10 +274,25 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   __shared__ int s_blk[kMaxPartTokens / 16];
   __shared__ int s_claim;   // next tile to hand out
 
-  const int p = blockIdx.x;
-  const int h0 = blockIdx.y * heads_per_wg;
+  // Which (partition, head group, sequence) this workgroup takes. With
+  // xcd_bit >= 0 the host found that bit xcd_bit of the head-group index
+  // is bit 8 of every kv slice address the group reads; the workgroup then
+  // takes an item whose bit 8 differs from its dispatch slot's parity (slot
+  // i runs on XCD i mod 8): items 2k and 2k+1 trade slots.
+  int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  if (xcd_bit >= 0) {
+    const int slot = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int item = slot ^ 1, half_y = gridDim.y >> 1;
+    int j = item >> 1;
+    p = j % (int)gridDim.x;
+    j /= (int)gridDim.x;
+    const int yh = j % half_y;
+    b = j / half_y;
+    hg = ((yh >> xcd_bit) << (xcd_bit + 1)) | ((item & 1) << xcd_bit) |
+         (yh & ((1 << xcd_bit) - 1));
+  }
+  const int h0 = hg * heads_per_wg;
   const int kvh = h0 / group;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int lrow = lane / CPR, lch = lane % CPR;
@@ -725,7 +740,9 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
                      a.max_blocks_per_seq, a.num_blocks, parts, part_tokens, a.k_scale,
                      a.v_scale, a.alibi, a.window_left, static_cast<uint8_t*>(a.app_k_cache),
                      static_cast<uint8_t*>(a.app_v_cache), a.new_key, a.new_value,
-                     a.slot_mapping);
+                     a.slot_mapping,
+                     decode_xcd_bit(a.num_kv_heads, group / hpw, D * (Q8 ? 1 : 2), a.k_cache,
+                                    a.v_cache));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || parts <= 1) return err;
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
