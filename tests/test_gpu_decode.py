@@ -130,6 +130,37 @@ def test_decode_group_larger_than_one_tile():
     check_decode(case)
 
 
+def test_decode_group_of_32_over_two_kv_heads():
+    """32 query heads per kv head over 2 kv heads: two 16-head workgroups per
+    kv head, so bit 1 of the head-group index is the kv head's parity, the
+    bit the launch pairs against its XCD."""
+    check_decode(wl.decode_case(911, [700, 33, 1600, 2048, 0, 1], 64, 2, 128, 32, "bf16"))
+
+
+def test_decode_pools_offset_by_256_bytes():
+    """Pools that start 256 bytes into their allocation (the workgroups then
+    keep the launch's own slot order): results still match the oracle."""
+    case = wl.decode_case(912, [2048, 1, 0, 777, 1500, 2047, 16, 1024] * 4, 32, 8, 128, 16, "f16")
+    dc = DeviceCase(case)
+
+    def shifted(t):
+        off = 256 // t.element_size()
+        flat = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+        view = flat[off:].view(t.shape)
+        view.copy_(t)
+        return view
+
+    k2, v2 = shifted(dc.k_cache), shifted(dc.v_cache)
+    assert k2.data_ptr() % 512 == 256 and v2.data_ptr() % 512 == 256
+    out = torch.empty_like(dc.q)
+    binding.paged_attention_decode(out, dc.q, k2, v2, dc.block_table, dc.seq_lens,
+                                   case.block_size, case.scale)
+    k, v = oracle_pools(case)
+    want = oracle.decode(case.q, k, v, case.block_table, case.seq_lens, case.block_size,
+                         case.scale, "f16")
+    assert max_abs_err(to_host(out, "f16"), want, "f16") <= ATOL["f16"]
+
+
 def _garbage_workspace(case):
     need = binding.paged_attention_decode_workspace_size(
         case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq, case.block_size)
