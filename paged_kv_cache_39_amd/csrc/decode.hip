@@ -733,6 +733,11 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
   const int group = a.num_q_heads / a.num_kv_heads;
   const int parts = decode_parts(a.max_blocks_per_seq, a.block_size, part_tokens);
   dim3 grid(parts, a.num_q_heads / hpw, a.num_seqs);
+  // the kernel forms the linear slot index in 32 bits
+  const bool slots_fit = (long long)parts * grid.y * grid.z < (1LL << 31);
+  const int xcd_bit = slots_fit ? decode_xcd_bit(a.num_kv_heads, group / hpw, D * (Q8 ? 1 : 2),
+                                                 a.k_cache, a.v_cache)
+                                : -1;
   launch_kernel((decode_mfma_kernel<Ty, D, WAVES, TT, Q8, EXT, APP>), grid, dim3(WAVES * kWave), 0,
                      stream, static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                      a.k_cache, a.v_cache, a.block_table, a.context_lens, a.ws_ml, a.ws_o,
@@ -740,9 +745,7 @@ static hipError_t launch_mfma_cfg(const DecodeArgs& a, hipStream_t stream, int h
                      a.max_blocks_per_seq, a.num_blocks, parts, part_tokens, a.k_scale,
                      a.v_scale, a.alibi, a.window_left, static_cast<uint8_t*>(a.app_k_cache),
                      static_cast<uint8_t*>(a.app_v_cache), a.new_key, a.new_value,
-                     a.slot_mapping,
-                     decode_xcd_bit(a.num_kv_heads, group / hpw, D * (Q8 ? 1 : 2), a.k_cache,
-                                    a.v_cache));
+                     a.slot_mapping, xcd_bit);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || parts <= 1) return err;
   return launch_reduce<Ty, D>(a, stream, log2_bs, parts, part_tokens);
