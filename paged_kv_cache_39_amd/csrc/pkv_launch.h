@@ -71,26 +71,25 @@ inline bool decode_fine_ok(long long num_seqs, long long num_q_heads, int max_bl
          16LL * kNumCUs;
 }
 // Decode workgroups are dispatched round-robin over the 8 XCDs (slot i on
-// XCD i mod 8). Measured, workgroups stream faster when bit 8 of the
-// addresses they read differs from their XCD's parity than when the two
-// agree: the LLaMA-7B-shaped decode 46.3 against 47.8 us, the long-context
-// one 331 against 335 us (the ragged GQA batch, bound by its longest rows
-// rather than by the chip's bandwidth, 0.5-0.8 us slower).
-// A workgroup reads one kv head's D-element slices; when a slice is at most
-// 256 bytes, both pool bases are 512-byte aligned and the kv head count
-// keeps every row a multiple of 512 bytes, bit 8 of each slice address is
-// bit log2(256 / slice) of the kv head index. Returns that bit's position in
-// the head-group index (head groups per kv head must be a power of two), or
-// -1 when the layout does not fix it.
+// XCD i mod 8). Measured with 256-byte kv slices (D = 128, 16-bit cache),
+// workgroups stream faster when bit 8 of the addresses they read differs
+// from their XCD's parity than when the two agree: the LLaMA-7B-shaped
+// decode 46.3 against 47.8 us, the long-context one 331 against 335 us (the
+// ragged GQA batch, bound by its longest rows rather than by the chip's
+// bandwidth, 0.5-0.8 us slower). Over the int8 cache (128-byte slices)
+// pairing bit 8 or bit 7 that way was 0.5 us slower than not pairing, so
+// only 256-byte slices are paired. When both pool bases are 512-byte
+// aligned and the kv head count is even (rows a multiple of 512 bytes), bit
+// 8 of every slice address is the kv head's parity. Returns that bit's
+// position in the head-group index (head groups per kv head must be a power
+// of two), or -1.
 inline int decode_xcd_bit(int num_kv_heads, int groups_per_kv_head, int slice_bytes,
                           const void* k_cache, const void* v_cache) {
-  if (slice_bytes <= 0 || slice_bytes > 256 || (256 % slice_bytes) != 0) return -1;
+  if (slice_bytes != 256 || num_kv_heads % 2 != 0) return -1;
   if (groups_per_kv_head <= 0 || (groups_per_kv_head & (groups_per_kv_head - 1)) != 0) return -1;
   if ((reinterpret_cast<uintptr_t>(k_cache) & 511) || (reinterpret_cast<uintptr_t>(v_cache) & 511))
     return -1;
-  const int kv_bit = __builtin_ctz(256 / slice_bytes);
-  if (num_kv_heads % (2 << kv_bit) != 0) return -1;
-  return kv_bit + __builtin_ctz(groups_per_kv_head);
+  return __builtin_ctz(groups_per_kv_head);
 }
 
 inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size,
