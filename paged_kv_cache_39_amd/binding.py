@@ -87,12 +87,13 @@ def lib() -> ctypes.CDLL:
         L.paged_attention_varlen_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                                 i32, i32, i64, i32, i32, i32, i32, i32, i64, i32,
                                                 vp]
+        L.paged_attention_varlen_ex.restype = ctypes.c_int
         L.paged_attention_varlen_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         L.paged_attention_varlen_workspace_size.restype = sz
         L.paged_attention_varlen_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32,
                                                    i64, i32, i32, i32, i32, i32, i64, i32, vp,
                                                    sz, vp]
-        L.paged_attention_varlen_ex.restype = ctypes.c_int
+        L.paged_attention_varlen_split.restype = ctypes.c_int
         L.paged_kv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
         L.paged_kv_copy_blocks.restype = ctypes.c_int
         L.pkv_bm_create.argtypes = [i64, i32]
@@ -195,10 +196,15 @@ _ws_cache = {}
 
 
 def _workspace(nbytes, device, stream):
+    """The cached workspace of (device, stream), grown when too small. It is
+    allocated with `stream` current, so the caching allocator ties the block
+    to the stream the kernels run on: a replaced buffer is not handed to
+    another allocation until that stream's work on it is done."""
     key = (device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 

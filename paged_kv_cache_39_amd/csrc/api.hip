@@ -71,14 +71,16 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
     return PKV_ERR_NULL;
+  // the one-dimensional grid: (query tiles [+ split chunk slots]) x kv heads
+  const int64_t splits =
+      split ? pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits : 1;
+  const int64_t wgs =
+      pkv::varlen_tiles(total_q, num_seqs, num_q_heads / num_kv_heads) * splits * num_kv_heads;
+  if (wgs > INT32_MAX) return PKV_ERR_SHAPE;
   if (split) {
     const size_t need = paged_attention_varlen_workspace_size(
         num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-    const int64_t wgs = pkv::varlen_tiles(total_q, num_seqs, num_q_heads / num_kv_heads) *
-                        pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits *
-                        num_kv_heads;
-    if (wgs > INT32_MAX) return PKV_ERR_SHAPE;
   }
 
   pkv::VarlenArgs a;

@@ -248,10 +248,22 @@ struct MfLds {
 // decode as long as no other sequence of the call reads that slot (a
 // sequence's last block is its own). Over an int8 cache (Q8) the new row is quantised with the kv head's
 // scales first, to the codes the int8 write would store.
+// The pool as the kernel reads it. Only the fused-write instances (APP)
+// also store into it (through app_k_cache / app_v_cache, the same buffers),
+// so only there may the read pointers not be restrict-qualified.
+template <bool APP>
+struct PoolRead {
+  using type = const void* __restrict__;
+};
+template <>
+struct PoolRead<true> {
+  using type = const void*;
+};
+
 template <class Ty, int D, int WAVES, int TT, bool Q8, bool EXT, bool APP>
 __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
-    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    typename PoolRead<APP>::type k_cache, typename PoolRead<APP>::type v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, float scale_log2, int num_q_heads,
     int num_kv_heads, int group, int heads_per_wg, int log2_bs, int max_blocks_per_seq,

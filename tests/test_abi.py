@@ -203,6 +203,9 @@ def test_varlen_validation(L):
     assert varlen(L, cu=None) == PKV_ERR_NULL
     assert varlen(L, sl=None) == PKV_ERR_NULL
     assert varlen(L, tq=0, q=None) == PKV_OK
+    # grid of (query tiles) x kv heads past 2^31 - 1 workgroups
+    assert varlen(L, tq=2**30 - 1, hq=4096, hkv=4096) == PKV_ERR_SHAPE
+    assert varlen(L, tq=2**30 - 1, hq=4096, hkv=4096, causal=0) == PKV_ERR_SHAPE
 
 
 def varlen_split(L, ws=FAKE, wsb=1 << 40, **kw):

@@ -93,7 +93,5 @@ def test_split_matches_plain_call():
 
 def test_split_mixed_batch_named_workload():
     """24 decode rows, 6 four-token decodes and 2 chunked prefills over
-    cached prefixes up to 4096 keys, bs 16: every query row of four heads."""
-    case = wl.workload(6)
-    rows = [(r, h) for r in range(case.q.shape[0]) for h in (0, 7, 18, 31)]
-    check_split(case, rows=rows)
+    cached prefixes up to 4096 keys, bs 16: every query row of every head."""
+    check_split(wl.workload(6))

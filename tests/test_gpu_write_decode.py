@@ -147,13 +147,11 @@ def test_write_decode_long_partition_plans(lens, part):
 
 
 def test_write_decode_llama7b_shape():
-    # the LLaMA-7B-shaped decode step (8 x 2048, 32/32 heads, fp16), output
-    # checked on sampled (sequence, head) pairs, the pool everywhere
+    # the LLaMA-7B-shaped decode step (8 x 2048, 32/32 heads, fp16) in the
+    # launch configuration the benchmark times: every (sequence, head)
+    # output and the whole pool checked
     case = wl.workload(2)
-    rng = np.random.default_rng(0)
-    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 8, 12), rng.integers(0, 32, 12))]
-    pairs += [(0, 0), (7, 31)]
-    check_step(case, pairs=pairs)
+    check_step(case)
 
 
 def test_write_decode_fine_partitions():
