@@ -66,7 +66,8 @@ typedef enum {
   PKV_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
   PKV_ERR_HIP = -6,         /* the HIP runtime rejected a launch */
   PKV_ERR_NO_BLOCKS = -7,   /* block manager: not enough free blocks */
-  PKV_ERR_PENDING_COPY = -8 /* block manager: take and apply pending block copies first */
+  PKV_ERR_PENDING_COPY = -8, /* block manager: take and apply pending block copies first */
+  PKV_ERR_SCRATCH = -9       /* paged_kv_write_decode_noalloc: partials exceed its scratch */
 } pkv_status;
 
 /*
@@ -173,6 +174,36 @@ int paged_kv_write_decode(void* out, const void* q, void* k_cache, void* v_cache
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_kv_write_decode_noalloc -- paged_kv_write_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, semantics and results as paged_kv_write_decode (the same
+ * kernels), without the workspace pair: the split-KV partials go to a
+ * device array that the library holds, PKV_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * on each GPU it runs on, from the first call on that GPU until the process
+ * ends. That first call looks the array's address up (hipGetSymbolAddress,
+ * for the device of `stream`); no call allocates or frees device or host
+ * memory. Calls whose partials need more than the array,
+ * paged_attention_decode_workspace_size(...) > PKV_NOALLOC_SCRATCH_BYTES,
+ * return PKV_ERR_SCRATCH and launch nothing.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's partials (each call writes every partial it reads, so nothing
+ * needs clearing). Calls that may overlap on one GPU -- on different
+ * streams, or from different host threads without ordering -- race on it
+ * and must be serialised by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_kv_write_decode_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                                  const void* key, const void* value,
+                                  const int32_t* slot_mapping, const int32_t* block_table,
+                                  const int32_t* context_lens, int32_t block_size, float scale,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
  * paged_attention_varlen -- packed variable-length (prefill) attention over

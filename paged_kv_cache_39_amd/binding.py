@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_float, i32, i32, i32, i32, i32, i64, i32,
                                             vp, sz, vp]
         L.paged_kv_write_decode.restype = ctypes.c_int
+        L.paged_kv_write_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                    ctypes.c_float, i32, i32, i32, i32, i32, i64,
+                                                    i32, vp]
+        L.paged_kv_write_decode_noalloc.restype = ctypes.c_int
         L.paged_kv_write_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  i32, ctypes.c_float, i32, i32, i32, i32, i32,
                                                  i64, i32, vp, sz, vp]
@@ -276,6 +280,40 @@ def paged_kv_write_decode(out, q, k_cache, v_cache, key, value, slot_mapping, bl
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
         _ptr(slot_mapping), _ptr(block_table), _ptr(context_lens), bs, float(scale), bsz, hq, hkv,
         d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes, _stream(s)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_kv_write_decode_noalloc(out, q, k_cache, v_cache, key, value, slot_mapping,
+                                  block_table, context_lens, block_size, scale, stream=None):
+    """paged_kv_write_decode without a workspace: the split-KV partials use
+    the library's own per-GPU scratch (NOALLOC_SCRATCH_BYTES), so the call
+    allocates nothing. Calls that overlap on one GPU race on that scratch."""
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("key", key), ("value", value)):
+        _need_gpu(n, t)
+    for n, t in (("slot_mapping", slot_mapping), ("block_table", block_table),
+                 ("context_lens", context_lens)):
+        _need_gpu(n, t, torch.int32)
+    nb, bs, hkv, d = _pool_dims(k_cache, v_cache)
+    if bs != block_size:
+        raise ValueError("block_size does not match k_cache.shape[1]")
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape:
+        raise ValueError("q/out must be [num_seqs, Hq, D]")
+    for t in (q, out, key, value):
+        if t.dtype != k_cache.dtype:
+            raise TypeError("q/out/key/value dtype must match the pool")
+    bsz, hq, _ = q.shape
+    if key.shape != (bsz, hkv, d) or value.shape != key.shape or slot_mapping.shape != (bsz,):
+        raise ValueError("key/value must be [num_seqs, Hkv, D], slot_mapping [num_seqs]")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or context_lens.shape != (bsz,):
+        raise ValueError("block_table must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _check("paged_kv_write_decode_noalloc", lib().paged_kv_write_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
+        _ptr(slot_mapping), _ptr(block_table), _ptr(context_lens), bs, float(scale), bsz, hq, hkv,
+        d, block_table.shape[1], nb, _code(q), _stream(s)))
 
 
 def paged_attention_varlen(out, q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,

@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 #include "pagedkv.h"
 #include "pkv_launch.h"
 
@@ -47,6 +49,105 @@ int decode_num_parts(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
 }
 
 }  // namespace
+
+// Split-KV scratch of the no-allocation decode step: one copy per GPU the
+// library runs on (the code object's global, allocated when the runtime
+// loads the library's kernels onto a device and held until the process
+// ends). In host code `scratch` names a host-side stand-in; the device
+// address of a GPU's copy comes from hipGetSymbolAddress with that GPU
+// current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The copy of `scratch` on the device that `stream` launches on (the current
+// device for the null stream), looked up once per device with that device
+// current; NULL if the runtime reports an error.
+void* scratch_for_stream(hipStream_t stream) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (err != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+// The fused decode step; with `noalloc` the partials go to the library's
+// scratch instead of the caller's workspace.
+static int write_decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                             const void* key, const void* value, const int32_t* slot_mapping,
+                             const int32_t* block_table, const int32_t* context_lens,
+                             int32_t block_size, float scale, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             bool noalloc) {
+  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !key || !value || !slot_mapping || !block_table ||
+      !context_lens)
+    return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                            max_blocks_per_seq, block_size);
+  if (noalloc) {
+    // the split-KV partials go to this device's copy of `scratch`
+    if (need > kScratchBytes) return PKV_ERR_SCRATCH;
+    if (need > 0) {
+      workspace = scratch_for_stream(static_cast<hipStream_t>(stream));
+      if (!workspace) return PKV_ERR_HIP;
+      workspace_bytes = kScratchBytes;
+    }
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.dtype = dtype;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
+      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  a.app_k_cache = k_cache;
+  a.app_v_cache = v_cache;
+  a.new_key = key;
+  a.new_value = value;
+  a.slot_mapping = slot_mapping;
+  hipError_t err = pkv::launch_write_decode(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
 
 static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
                            const void* k_cache, const void* v_cache,
@@ -128,6 +229,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_HIP: return "the HIP runtime rejected a launch";
     case PKV_ERR_NO_BLOCKS: return "not enough free cache blocks";
     case PKV_ERR_PENDING_COPY: return "pending block copies must be taken and applied first";
+    case PKV_ERR_SCRATCH:
+      return "the split-KV partials need more than the no-allocation call's scratch";
     default: return "unknown status";
   }
 }
@@ -231,48 +334,23 @@ int paged_kv_write_decode(void* out, const void* q, void* k_cache, void* v_cache
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype)) return PKV_ERR_DTYPE;
-  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
-  int st = check_pool(num_kv_heads, head_dim, block_size, num_blocks);
-  if (st != PKV_OK) return st;
-  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
-  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
-  if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !key || !value || !slot_mapping || !block_table ||
-      !context_lens)
-    return PKV_ERR_NULL;
-  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
-                                                            max_blocks_per_seq, block_size);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return write_decode_impl(out, q, k_cache, v_cache, key, value, slot_mapping, block_table,
+                           context_lens, block_size, scale, num_seqs, num_q_heads, num_kv_heads,
+                           head_dim, max_blocks_per_seq, num_blocks, dtype, workspace,
+                           workspace_bytes, stream, false);
+}
 
-  pkv::DecodeArgs a;
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.scale = scale;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
-  a.app_k_cache = k_cache;
-  a.app_v_cache = v_cache;
-  a.new_key = key;
-  a.new_value = value;
-  a.slot_mapping = slot_mapping;
-  hipError_t err = pkv::launch_write_decode(a, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+int paged_kv_write_decode_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                                  const void* key, const void* value,
+                                  const int32_t* slot_mapping, const int32_t* block_table,
+                                  const int32_t* context_lens, int32_t block_size, float scale,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, void* stream) {
+  return write_decode_impl(out, q, k_cache, v_cache, key, value, slot_mapping, block_table,
+                           context_lens, block_size, scale, num_seqs, num_q_heads, num_kv_heads,
+                           head_dim, max_blocks_per_seq, num_blocks, dtype, nullptr, 0, stream,
+                           true);
 }
 
 int paged_attention_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,

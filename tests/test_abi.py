@@ -15,6 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE = 0, -1, -2, -3
 PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = -4, -5, -6
+PKV_ERR_SCRATCH = -9
 
 
 def declared_functions():
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         s = binding.status_string(st)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"
@@ -124,6 +125,34 @@ def test_write_decode_validation(L):
     assert write_decode(L, ws=None) == PKV_ERR_WORKSPACE
     assert write_decode(L, wsb=need - 1) == PKV_ERR_WORKSPACE
     assert write_decode(L, b=0, q=None, key=None) == PKV_OK     # empty batch
+
+
+def write_decode_noalloc(L, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, key=FAKE, value=FAKE, slots=FAKE, bt=FAKE,
+             ctx=FAKE, bs=16, scale=0.1, b=2, hq=8, hkv=2, d=128, maxblk=64, nb=256, dtype=2)
+    a.update(kw)
+    return L.paged_kv_write_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["key"],
+                                           a["value"], a["slots"], a["bt"], a["ctx"], a["bs"],
+                                           a["scale"], a["b"], a["hq"], a["hkv"], a["d"],
+                                           a["maxblk"], a["nb"], a["dtype"], None)
+
+
+def test_write_decode_noalloc_validation(L):
+    assert write_decode_noalloc(L, dtype=3) == PKV_ERR_DTYPE
+    assert write_decode_noalloc(L, hq=6, hkv=4) == PKV_ERR_SHAPE
+    assert write_decode_noalloc(L, d=80) == PKV_ERR_UNSUPPORTED
+    assert write_decode_noalloc(L, maxblk=0) == PKV_ERR_SHAPE
+    for name in ("out", "q", "k", "v", "key", "value", "slots", "bt", "ctx"):
+        assert write_decode_noalloc(L, **{name: None}) == PKV_ERR_NULL, name
+    assert write_decode_noalloc(L, b=0, q=None, key=None) == PKV_OK
+    # partials beyond the library's scratch: rejected before any device call
+    big = dict(b=64, hq=64, hkv=8, maxblk=1024, bs=128, nb=4096)
+    need = L.paged_attention_decode_workspace_size(64, 64, 128, 1024, 128)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert write_decode_noalloc(L, **big) == PKV_ERR_SCRATCH
+    # the long-context workload (4 x 131072 tokens, 64 query heads) fits
+    assert L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128) <= \
+        binding.NOALLOC_SCRATCH_BYTES
 
 
 def test_write_decode_int8_validation(L):
