@@ -393,6 +393,23 @@ def main():
                              "partition_tokens": binding.decode_partition_tokens(
                                  m.num_seqs, m.num_q_heads, m.num_kv_heads,
                                  m.max_blocks_per_seq, m.block_size, tdt(m.dtype))}
+            if c == 5:
+                # the same call with the workload's stated 512-token
+                # partitions (4-wave workgroups + the reduce) instead of the
+                # launch plan's
+                binding.decode_partition_override(512)
+                try:
+                    ms5, kms5 = time_calls(lambda: run_decode(m, tt), n_extra)
+                finally:
+                    binding.decode_partition_override(0)
+                mu5 = statistics.mean(ms5)
+                extra[m.name]["partition_512"] = {
+                    "us": round(mu5 * 1e3, 2),
+                    "gbs": round(m.decode_bytes() / (mu5 * 1e-3) / 1e9, 1),
+                    "hbm_peak_frac": round(m.decode_bytes() / (mu5 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                           4),
+                    "kernel_us": round(statistics.mean(kms5) * 1e3, 2),
+                    "partition_tokens": 512}
             if c == 3:
                 # the ragged batch's decode step too (write + attention): one
                 # fused call, and the two calls
@@ -647,9 +664,10 @@ def cpu_baseline():
     from paged_kv_cache_39_amd import workloads as wl
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
+        threadpool_limits = None
         threads = 1
     case = wl.workload(2)
     rows = case.new_token_rows
@@ -671,16 +689,36 @@ def cpu_baseline():
         dt = time.perf_counter() - t0
         if dt >= 10.0 or steps >= 200:
             break
-    kv_bytes = steps * sum(int(case.seq_lens[b]) for b, _ in pairs) * 2 * case.head_dim * 2
+    step_bytes = sum(int(case.seq_lens[b]) for b, _ in pairs) * 2 * case.head_dim * 2
+    kv_bytes = steps * step_bytes
+    # the same step with the BLAS pool held to one thread (the oracle's
+    # Python loops are single-threaded either way)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            s1 = 0
+            t1 = time.perf_counter()
+            while True:
+                k1, v1 = oracle.write_kv(k0, v0, case.key[rows], case.value[rows],
+                                         case.slot_mapping[rows], case.block_size)
+                oracle.decode(case.q, k1, v1, case.block_table, case.seq_lens, case.block_size,
+                              case.scale, case.dtype, pairs=pairs)
+                s1 += 1
+                d1 = time.perf_counter() - t1
+                if d1 >= 5.0 or s1 >= 100:
+                    break
+        single = {"value": round(s1 * step_bytes / d1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                  "steps": s1, "seconds": round(d1, 3), "us_per_step": round(d1 / s1 * 1e6, 1)}
     per_config = oracle_per_config()
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(threads), "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{steps} full decode steps of the LLaMA-7B-shaped batch, each an oracle "
                       f"KV write of the 8 new tokens then all {len(pairs)} (sequence, head) pairs "
                       f"over 2048 tokens; {dt:.2f} s",
             "us_per_step": round(dt / steps * 1e6, 1),
             "seconds": round(dt, 3),
             "affinity_cpus": len(os.sched_getaffinity(0)),
+            "single_thread": single,
             "per_config_seconds": per_config}
 
 

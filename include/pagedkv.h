@@ -431,6 +431,19 @@ int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32
  */
 int pkv_time_next_kernel(void* start_event, void* stop_event);
 
+/*
+ * pkv_decode_partition_override -- measurement and tuning hook. The calling
+ * thread's fp16 / bf16 decode calls (paged_attention_decode, _ex, _int8,
+ * paged_kv_write_decode and its int8 and no-allocation forms) cut every
+ * context into partitions of partition_tokens tokens (512, 1024, 2048 or
+ * 4096: 4-wave workgroups at 512, 8-wave ones above) instead of the launch
+ * plan's choice, until the thread calls it with 0. The split-KV workspace
+ * that paged_attention_decode_workspace_size reports covers every such
+ * value. The results are the same up to summation order. Returns PKV_OK,
+ * or PKV_ERR_SHAPE (and changes nothing) for any other value.
+ */
+int pkv_decode_partition_override(int32_t partition_tokens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_decode_partition_tokens.restype = i32
         L.pkv_time_next_kernel.argtypes = [vp, vp]
         L.pkv_time_next_kernel.restype = ctypes.c_int
+        L.pkv_decode_partition_override.argtypes = [i32]
+        L.pkv_decode_partition_override.restype = ctypes.c_int
         L.paged_kv_write_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64,
                                           i32, vp]
         L.paged_kv_write_int8.restype = ctypes.c_int
@@ -648,6 +650,14 @@ def paged_kv_write_decode_int8(out, q, k_cache, v_cache, key, value, k_scale, v_
         _ptr(v_scale), _ptr(slot_mapping), _ptr(block_table), _ptr(context_lens), bs,
         float(scale), bsz, hq, hkv, d, maxblk, nb, _code(q), _ptr(workspace), ws_bytes,
         _stream(s)))
+
+
+def decode_partition_override(partition_tokens: int) -> None:
+    """The calling thread's 16-bit decode calls use partitions of this many
+    tokens (512, 1024, 2048 or 4096) instead of the launch plan's; 0 restores
+    the plan (pkv_decode_partition_override)."""
+    _check("pkv_decode_partition_override", lib().pkv_decode_partition_override(
+        int(partition_tokens)))
 
 
 def time_next_kernel(start_event, stop_event) -> None:

@@ -16,7 +16,19 @@ KernelTiming& pending_timing() {
   thread_local KernelTiming t;
   return t;
 }
+int& decode_partition_override() {
+  thread_local int tokens = 0;
+  return tokens;
+}
 }  // namespace pkv
+
+int pkv_decode_partition_override(int32_t partition_tokens) {
+  if (partition_tokens != 0 && partition_tokens != 512 && partition_tokens != 1024 &&
+      partition_tokens != 2048 && partition_tokens != 4096)
+    return PKV_ERR_SHAPE;
+  pkv::decode_partition_override() = partition_tokens;
+  return PKV_OK;
+}
 
 int pkv_time_next_kernel(void* start_event, void* stop_event) {
   pkv::KernelTiming& t = pkv::pending_timing();

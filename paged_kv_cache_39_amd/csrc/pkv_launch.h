@@ -17,6 +17,10 @@ struct KernelTiming {
   hipEvent_t stop = nullptr;
 };
 KernelTiming& pending_timing();
+// Partition length the calling thread's 16-bit decode calls use instead of
+// the launch plan's (0: the plan decides; set by
+// pkv_decode_partition_override).
+int& decode_partition_override();
 
 // Every kernel of the library is launched through here.
 template <typename... Formals, typename... Actuals>
@@ -94,6 +98,8 @@ inline int decode_xcd_bit(int num_kv_heads, int groups_per_kv_head, int slice_by
 
 inline DecodePlan plan_decode(int num_seqs, int groups, int max_blocks_per_seq, int block_size,
                               bool fine_ok) {
+  const int forced = decode_partition_override();
+  if (forced > 0) return {forced >= 2 * kDecodePart ? 8 : 4, forced};
   const long long rows = (long long)num_seqs * groups;
   const long long max_ctx = (long long)max_blocks_per_seq * block_size;
   if (rows >= kNumCUs && max_ctx <= kDecodeWidePart) {

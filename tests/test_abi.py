@@ -342,3 +342,20 @@ def test_block_manager_exports(L):
 def test_time_next_kernel_without_events(L):
     # NULL, NULL cancels the hook; no HIP call is made
     assert L.pkv_time_next_kernel(None, None) == 0
+
+
+def test_decode_partition_override(L):
+    assert L.pkv_decode_partition_override(300) == PKV_ERR_SHAPE
+    assert L.pkv_decode_partition_override(8192) == PKV_ERR_SHAPE
+    # the long-context shape: the plan takes 4096-token partitions
+    assert L.pkv_decode_partition_tokens(4, 64, 8, 1024, 128, 2) == 4096
+    try:
+        for part in (512, 1024, 2048, 4096):
+            assert L.pkv_decode_partition_override(part) == PKV_OK
+            assert L.pkv_decode_partition_tokens(4, 64, 8, 1024, 128, 2) == part
+            # the workspace the size function reports covers the forced split
+            ws = L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128)
+            assert ws >= 4 * 64 * (131072 // part) * (128 + 2) * 4
+    finally:
+        assert L.pkv_decode_partition_override(0) == PKV_OK
+    assert L.pkv_decode_partition_tokens(4, 64, 8, 1024, 128, 2) == 4096

@@ -239,3 +239,22 @@ def test_decode_fine_partitions_for_small_problems(lens, hq, hkv, bs, part):
     assert binding.decode_partition_tokens(len(lens), hq, hkv, case.max_blocks_per_seq, bs,
                                            torch.bfloat16) == part
     check_decode(case)
+
+
+@pytest.mark.parametrize("part", [512, 1024, 2048, 4096])
+def test_decode_partition_override(part):
+    """Every partition length the override accepts, on a batch whose own plan
+    is one workgroup per whole context (so each forced length is a split)
+    and on the long-context-like GQA shape: same results up to rounding."""
+    lens = [1, 511, 512, 513, 2047, 2048, 1500, 0] * 8   # 512 rows of <= 2048 tokens
+    whole = wl.decode_case(960 + part, lens, 8, 8, 128, 16, "f16", spare=0.05)
+    long = wl.decode_case(970 + part, [9000, 4096, 4097, 1], 64, 8, 128, 128, "bf16")
+    binding.decode_partition_override(part)
+    try:
+        for case in (whole, long):
+            assert binding.decode_partition_tokens(
+                case.num_seqs, case.num_q_heads, case.num_kv_heads, case.max_blocks_per_seq,
+                case.block_size, torch.float16) == part
+            check_decode(case)
+    finally:
+        binding.decode_partition_override(0)
