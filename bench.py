@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the packed causal prefill workload (for counter runs)")
+    ap.add_argument("--prefill-workload", type=int, default=4, choices=(4, 6),
+                    help="with --prefill-only: the packed prefill (4) or the mixed batch (6)")
     return ap.parse_args()
 
 
@@ -174,7 +176,7 @@ def main():
 
     if args.prefill_only:
         # the packed causal prefill alone: W warm-up calls, then K timed calls
-        m = wl.workload(4, values=False)
+        m = wl.workload(args.prefill_workload, values=False)
         dtp = tdt(m.dtype)
         k = torch.randn(m.pool_shape(), dtype=dtp, device=dev)
         v = torch.randn_like(k)
@@ -195,9 +197,22 @@ def main():
             b.record()
         torch.cuda.synchronize()
         mu = statistics.mean([a.elapsed_time(b) for a, b in evs])
+        # the kernel alone: dispatch-recorded events, one call each
+        ke = KernelEvents(args.steps)
+        for i in range(args.steps):
+            evict()
+            ke.arm(binding, i)
+            binding.paged_attention_varlen(out, q, cu, k, v, bt, sl, True)
+        torch.cuda.synchronize()
+        kms = [ke.ms(i) for i in range(args.steps)]
+        ke.close()
+        km = statistics.mean(kms)
         fl = m.prefill_flops()
         print(json.dumps({"workload": m.name, "steps": args.steps, "us": round(mu * 1e3, 2),
-                          "tflops": round(fl / (mu * 1e-3) / 1e12, 2), "flops": fl}))
+                          "tflops": round(fl / (mu * 1e-3) / 1e12, 2), "flops": fl,
+                          "kernel_us": round(km * 1e3, 2),
+                          "kernel_us_min": round(min(kms) * 1e3, 2),
+                          "kernel_tflops": round(fl / (km * 1e-3) / 1e12, 2)}))
         return
 
     def decode_setup(meta):

@@ -168,6 +168,44 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
 }
 
+// Wave-wide reductions and scans of 32-bit integers that stay out of LDS:
+// DPP moves within each row of 16 lanes, then the four row results through
+// scalar registers (v_readlane). Every lane of the wave must be active; the
+// reductions return a wave-uniform value.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int lane_value(int x, int lane) {
+  return __builtin_amdgcn_readlane(x, lane);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp_i<kDppQuadPerm1032>(x);
+  x += dpp_i<kDppQuadPerm2301>(x);
+  x += dpp_i<kDppRowHalfMirror>(x);
+  x += dpp_i<kDppRowMirror>(x);
+  return lane_value(x, 0) + lane_value(x, 16) + lane_value(x, 32) + lane_value(x, 48);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_i<kDppQuadPerm1032>(x));
+  x = max(x, dpp_i<kDppQuadPerm2301>(x));
+  x = max(x, dpp_i<kDppRowHalfMirror>(x));
+  x = max(x, dpp_i<kDppRowMirror>(x));
+  return max(max(lane_value(x, 0), lane_value(x, 16)), max(lane_value(x, 32), lane_value(x, 48)));
+}
+// Inclusive prefix sum over the lanes: shifts right by 1, 2, 4, 8 within
+// each row (lanes whose source lies before the row start add 0), then the
+// totals of the preceding rows.
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  x += dpp_i<0x111>(x);   // row_shr:1
+  x += dpp_i<0x112>(x);   // row_shr:2
+  x += dpp_i<0x114>(x);   // row_shr:4
+  x += dpp_i<0x118>(x);   // row_shr:8
+  const int t0 = lane_value(x, 15), t1 = lane_value(x, 31), t2 = lane_value(x, 47);
+  const int lane = (int)__lane_id();
+  return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Asynchronous 16-byte global -> LDS copies per lane: lane l's 16 bytes land

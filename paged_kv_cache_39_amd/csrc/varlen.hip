@@ -59,12 +59,6 @@ __device__ __forceinline__ int seq_tiles(const int32_t* __restrict__ cu, int num
   return lq > 0 ? (lq + bq - 1) / bq : 0;
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
-}
-
 // sum_b min(nt_b, cap) over the batch (cap < 0: no cap). `nt0` holds the
 // count of sequence `lane` (the first 64 sequences, read once); further
 // sequences are read from memory.
@@ -75,7 +69,7 @@ __device__ __forceinline__ int tiles_below(const int32_t* __restrict__ cu, int n
     const int nt = seq_tiles(cu, num_seqs, bq, total_q, s0 + lane);
     sum += cap < 0 ? nt : min(nt, cap);
   }
-  return wave_sum(sum);
+  return wave_sum_i(sum);
 }
 
 // Locate query tile `t` of one kv head (tiles of `bq` query positions).
@@ -93,10 +87,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
   int lo = 0, hi = 1;
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
     const int nt = s0 == 0 ? nt0 : seq_tiles(cu, num_seqs, bq, total_q, s0 + lane);
-    int m = nt;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, kWave));
-    hi = max(hi, m + 1);
+    hi = max(hi, wave_max_i(nt) + 1);
   }
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -113,7 +104,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
       unsigned long long m = has;   // position of the r-th set bit
       for (int k = 0; k < r; ++k) m &= m - 1;
       const int first = __builtin_ctzll(m);
-      const int ntile = __shfl(nt, first, kWave);
+      const int ntile = lane_value(nt, first);
       seq = s0 + first;
       q0 = (ntile - 1 - j) * bq;
       return true;
@@ -181,7 +172,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
       meta(s0, lq, lk);
       c += tiles_with_work(w, lq, lk, bq, bq_log2, causal);
     }
-    return wave_sum(c);
+    return wave_sum_i(c);
   };
   if (g >= count(0)) return false;
   int wmax = 0;
@@ -190,8 +181,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     meta(s0, lq, lk);
     wmax = max(wmax, (lk + kVlBN - 1) / kVlBN);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, kWave));
+  wmax = wave_max_i(wmax);
   int lo = 0, hi = wmax + 1;   // count(lo) > g >= count(hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -204,18 +194,13 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     meta(s0, lq, lk);
     const int ge = tiles_with_work(lo, lq, lk, bq, bq_log2, causal);
     const int c = ge - tiles_with_work(lo + 1, lq, lk, bq, bq_log2, causal);
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
+    const int incl = wave_incl_scan_i(c);
+    const int total = lane_value(incl, kWave - 1);
     if (r < total) {
       const unsigned long long hit = __ballot(incl - c <= r && r < incl);
       const int L = __builtin_ctzll(hit);
-      const int nt = div_bq(__shfl(lq, L, kWave) + bq - 1, bq, bq_log2);
-      const int t = nt - __shfl(ge, L, kWave) + (r - __shfl(incl - c, L, kWave));
+      const int nt = div_bq(lane_value(lq, L) + bq - 1, bq, bq_log2);
+      const int t = nt - lane_value(ge, L) + (r - lane_value(incl - c, L));
       seq = s0 + L;
       q0 = t * bq;
       return true;
@@ -305,7 +290,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     // monotone in its position, so those tiles go by rank from the end
     bool found;
     if (SPLIT && extra) {   // the last tile of sequence xseq
-      const int ntx = xseq < kWave ? __shfl(nt0, xseq, kWave)
+      const int ntx = xseq < kWave ? lane_value(nt0, xseq)
                                    : seq_tiles(cu_seqlens_q, num_seqs, bq, total_q, xseq);
       found = ntx > 0;
       seq = xseq;
@@ -319,9 +304,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     }
     if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
-      r0 = __shfl(my_r0, seq, kWave);
-      lq_ = __shfl(my_lq, seq, kWave);
-      lk_ = __shfl(my_lk, seq, kWave);
+      r0 = lane_value(my_r0, seq);
+      lq_ = lane_value(my_lq, seq);
+      lk_ = lane_value(my_lk, seq);
     } else if (seq >= kWave) {
       r0 = max(0, min(cu_seqlens_q[seq], total_q));
       lq_ = max(0, min(cu_seqlens_q[seq + 1], total_q) - r0);
