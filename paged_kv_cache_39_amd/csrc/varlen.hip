@@ -380,8 +380,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // block address (from a scalar load of the block id) plus a loop-invariant
   // 32-bit lane offset. In the last tile, keys past Lk fetch the last valid
   // key instead (finite values whose probabilities are masked to zero).
-  // per-lane parts (loop invariant): row within the copy, swizzled source
-  // chunk, kv head -> byte offset from the copy's first row
+  // per-lane parts (loop invariant): row of the tile, swizzled source
+  // chunk, kv head -> byte offset from the tile's first row, so that every
+  // copy of a tile that lies in one block shares one scalar base address
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;
   uint32_t voffk_[LPT], voffv_[LPT];
   int lrow_[LPT], loffk_[LPT], loffv_[LPT];
@@ -392,36 +393,50 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     // the lane's LDS slot is lane % spr; it holds chunk slot ^ f(row)
     loffk_[j] = kvh * D + L::slot_k(lrow_[j], lane % L::spr) * 8;
     loffv_[j] = kvh * D + L::slot_v(lrow_[j], lane % L::spr) * 8;
-    voffk_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loffk_[j] * 2u;
-    voffv_[j] = (uint32_t)(lane / L::spr) * row_bytes + (uint32_t)loffv_[j] * 2u;
+    voffk_[j] = (uint32_t)lrow_[j] * row_bytes + (uint32_t)loffk_[j] * 2u;
+    voffv_[j] = (uint32_t)lrow_[j] * row_bytes + (uint32_t)loffv_[j] * 2u;
   }
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k_cache);
   const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(v_cache);
   const uint32_t lds_kv = lds_address(s_kv);
-  auto block_of = [&](int i) {   // validated block id of table entry i (wave-uniform)
-    const int blk = __builtin_amdgcn_readfirstlane(bt_row[i]);
-    return (blk >= 0 && blk < num_blocks) ? blk : 0;
+  // the pool's block count fits 32 bits (num_blocks * block_size is checked
+  // against INT32_MAX by the caller)
+  const uint32_t nblocks32 = (uint32_t)num_blocks;
+  auto valid_block = [&](int blk) {   // out-of-range ids read block 0
+    return (uint32_t)blk < nblocks32 ? blk : 0;
   };
+  // byte offset of pool row r (a 32-bit row index) as a signed 64-bit value
+  auto row_offset = [&](int r) { return (int64_t)r * (int64_t)row_bytes; };
   auto stage = [&](int st, int kv0) {
     const uint32_t lds_st = lds_kv + (uint32_t)(st * L::stageB);
+    const int i0 = kv0 >> log2_bs;
     if (kv0 + kVlBN <= lk) {
-      if (bs >= kVlBN) {   // the whole tile lies in one block
-        const size_t base =
-            ((size_t)block_of(kv0 >> log2_bs) * bs + (kv0 & (bs - 1))) * (size_t)row_bytes;
+      if (bs >= kVlBN) {   // the whole tile lies in one block: one base
+        const int blk = valid_block(__builtin_amdgcn_readfirstlane(bt_row[i0]));
+        const int64_t base = row_offset(blk * bs + (kv0 & (bs - 1)));
+        const uint8_t* kb = kbytes + base;
+        const uint8_t* vb = vbytes + base;
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
           const int rbase = (j * kVlWaves + wave) * RPI;
-          const size_t src = base + (size_t)rbase * row_bytes;
-          async_copy16_to_lds(kbytes + src, voffk_[j], lds_st + rbase * L::rowB);
-          async_copy16_to_lds(vbytes + src, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
+          async_copy16_to_lds(kb, voffk_[j], lds_st + rbase * L::rowB);
+          async_copy16_to_lds(vb, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
         }
       } else {
+        // copy j covers rows rbase .. rbase+RPI-1, all in table entry
+        // i0 + rbase / bs (kv0 is a multiple of the tile, hence of bs); the
+        // lane offsets count rows from the tile's first key, so the base is
+        // that block's start less the block's first row within the tile.
+        // The ids are requested together, one wait for all.
+        int ids[LPT];
+#pragma unroll
+        for (int j = 0; j < LPT; ++j)
+          ids[j] = __builtin_amdgcn_readfirstlane(
+              bt_row[i0 + (((j * kVlWaves + wave) * RPI) >> log2_bs)]);
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
           const int rbase = (j * kVlWaves + wave) * RPI;
-          const int key = kv0 + rbase;
-          const size_t src = ((size_t)block_of(key >> log2_bs) * bs + (key & (bs - 1))) *
-                             (size_t)row_bytes;
+          const int64_t src = row_offset(valid_block(ids[j]) * bs - (rbase & ~(bs - 1)));
           async_copy16_to_lds(kbytes + src, voffk_[j], lds_st + rbase * L::rowB);
           async_copy16_to_lds(vbytes + src, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
         }
@@ -431,10 +446,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     // the tile's keys span at most four blocks (block_size >= 16): their ids
     // come from scalar loads (a per-lane load would make the next vmcnt wait
     // cover the copies in flight)
-    const int i0 = kv0 >> log2_bs;
     int ids[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ids[e] = block_of(min(i0 + e, max_blocks_per_seq - 1));
+    for (int e = 0; e < 4; ++e)
+      ids[e] = valid_block(
+          __builtin_amdgcn_readfirstlane(bt_row[min(i0 + e, max_blocks_per_seq - 1)]));
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int rbase = (j * kVlWaves + wave) * RPI;
