@@ -329,12 +329,14 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // rows of this lane: r = wave*32 + mt*16 + l16 -> (query i = r / group, head r % group)
   int q_pos[2], head[2], lim[2];
   bool row_ok[2];
+  // (shifts when the group size is a power of two, the usual case)
+  const int group_log2 = (group & (group - 1)) == 0 ? __builtin_ctz(group) : -1;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int r = wave * kVlRowsWave + mt * 16 + l16;
-    const int i = r / group;
+    const int i = group_log2 >= 0 ? r >> group_log2 : r / group;
     q_pos[mt] = q0 + i;
-    head[mt] = kvh * group + r % group;
+    head[mt] = kvh * group + (r - i * group);
     row_ok[mt] = (i < bq) && (q_pos[mt] < lq);
     lim[mt] = row_ok[mt] ? (causal ? min(lk - 1, q_pos[mt] + delta) : lk - 1) : -1;
   }
@@ -620,6 +622,8 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         }
         const bool grow = (mx[0] > m_use[0] + kRescale) || (mx[1] > m_use[1] + kRescale);
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare
+          // before the first half is accumulated the sums are still zero
+          const bool rescale = it > 0 || hh > 0;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
             float m = mx[mt];
@@ -629,9 +633,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
             const float alpha = fast_exp2(m_use[mt] - safe_max_ref(mnew));
             m_use[mt] = mnew;
             nref[mt] = -safe_max_ref(mnew);
-            lacc[mt] *= alpha;
+            if (rescale) {
+              lacc[mt] *= alpha;
 #pragma unroll
-            for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
+              for (int nd = 0; nd < ND; ++nd) acc[mt][nd] *= alpha;
+            }
           }
         }
         u32x4_t pb[2];
