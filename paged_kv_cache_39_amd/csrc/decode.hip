@@ -489,8 +489,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
         sv[n][i] = vis ? x : -INFINITY;
         mx = fmaxf(mx, sv[n][i]);
       }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float mnew = fmaxf(m_run, mx);
     const float mref = safe_max_ref(mnew);
     const float alpha = fast_exp2(m_run - mref);
@@ -596,8 +595,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   }
 
   // ---- merge lanes (the 4 lane groups) and waves ----
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
+  l_run = sum_xor32(sum_xor16(l_run));
   __syncthreads();  // every wave is done with its K/V tiles
   float* s_ml = reinterpret_cast<float*>(s_mem);                 // [wave][16][2]
   float* s_o = s_ml + WAVES * 16 * 2;                            // [wave][16][oRow]

@@ -168,6 +168,32 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
 }
 
+// Max / sum with the lane 16 (resp. 32) positions away through gfx950's
+// v_permlane16_swap / v_permlane32_swap, without LDS: swapping a register
+// with itself leaves every lane i holding its own value and lane
+// i ^ 16 (i ^ 32)'s, in either order (measured on the GPU), so the max and
+// the sum of the two results are those of the pair.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-wide reductions and scans of 32-bit integers that stay out of LDS:
 // DPP moves within each row of 16 lanes, then the four row results through
 // scalar registers (v_readlane). Every lane of the wave must be active; the
@@ -315,7 +341,30 @@ struct Mma<F16> {
 // as Ty (two 16-byte chunks, 8 values each). Exact: |code| <= 127 has at
 // most 7 significant bits.
 template <class Ty>
-__device__ __forceinline__ void widen_i8x16(const u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+__device__ __forceinline__ void widen_i8x16(const u32x4_t c, u32x4_t& lo, u32x4_t& hi);
+// fp16: two codes at a time. A code x placed as the byte (x + 128) under the
+// exponent bits of 1024.0 gives the fp16 number 1024 + 128 + x exactly (ten
+// mantissa bits), so one packed subtraction of 1152 yields x exactly.
+template <>
+__device__ __forceinline__ void widen_i8x16<F16>(const u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t r[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // bytes 0,1 (2,3) of the word into bits 7:0 and 23:16, the rest zero
+    const uint32_t p01 = __builtin_amdgcn_perm(0u, c[w], 0x0C010C00u);
+    const uint32_t p23 = __builtin_amdgcn_perm(0u, c[w], 0x0C030C02u);
+    const f16x2_t bias = {(_Float16)1152.f, (_Float16)1152.f};
+    const f16x2_t a = __builtin_bit_cast(f16x2_t, (p01 ^ 0x00800080u) | 0x64006400u) - bias;
+    const f16x2_t b = __builtin_bit_cast(f16x2_t, (p23 ^ 0x00800080u) | 0x64006400u) - bias;
+    r[2 * w] = __builtin_bit_cast(uint32_t, a);
+    r[2 * w + 1] = __builtin_bit_cast(uint32_t, b);
+  }
+  lo = u32x4_t{r[0], r[1], r[2], r[3]};
+  hi = u32x4_t{r[4], r[5], r[6], r[7]};
+}
+template <>
+__device__ __forceinline__ void widen_i8x16<BF16>(const u32x4_t c, u32x4_t& lo, u32x4_t& hi) {
+  using Ty = BF16;
   uint32_t r[8];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
