@@ -16,7 +16,10 @@ import threading
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PAGEDKV_LIBRARY names another build of the same library to load (the
+# host-sanitizer build in CPU test runs); by default the in-tree build.
+_LIB_PATH = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 _lib = None
 _lock = threading.Lock()
 

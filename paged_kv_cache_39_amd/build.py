@@ -1,6 +1,13 @@
 """Build libpagedkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_39_amd.build          # build (always recompiles)
+    python -m paged_kv_cache_39_amd.build              # build (always recompiles)
+    python -m paged_kv_cache_39_amd.build --sanitize   # host-side ASan + UBSan build
+
+The sanitizer build (libpagedkv_sanitize.so) instruments the host code only
+(argument validation, workspace layout, the block manager); its device code
+is the regular build's. It is for CPU test runs: load it through the
+PAGEDKV_LIBRARY environment variable with clang's ASan runtime preloaded
+(see sanitizer_env()).
 """
 
 from __future__ import annotations
@@ -14,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
+SANITIZE_LIB = os.path.join(PKG, "libpagedkv_sanitize.so")
 SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "varlen.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
@@ -39,11 +47,41 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpagedkv.so (always recompiles)."""
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", out_tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+# host-only instrumentation: every sanitizer flag goes to the host pass
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+                  "-fno-omit-frame-pointer", "-shared-libasan", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime that the sanitizer build links."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's ASan runtime (libclang_rt.asan-x86_64.so) not found")
+    return path
+
+
+def sanitizer_env() -> dict:
+    """Environment for a Python process that loads the sanitizer build."""
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = asan_runtime()
+    env["PAGEDKV_LIBRARY"] = SANITIZE_LIB
+    # the interpreter itself is not instrumented: its own allocations are
+    # not leak-checked; UBSan findings abort with a report
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return env
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source into libpagedkv.so, or with `sanitize` into the
+    host-instrumented libpagedkv_sanitize.so (always recompiles)."""
+    lib = SANITIZE_LIB if sanitize else LIB
+    out_tmp = lib + ".tmp"
+    cmd = [hipcc(), *compile_flags(), *(SANITIZE_FLAGS if sanitize else []), "-shared", "-o",
+           out_tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,9 +92,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(out_tmp, LIB)
-    return LIB
+    os.replace(out_tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    print(build(verbose="-q" not in sys.argv, sanitize="--sanitize" in sys.argv))
