@@ -99,8 +99,10 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
  * context partition, fp32. Partitions are counted at 512 tokens, or at 128
  * tokens for small problems (num_seqs x num_q_heads x ceil(max_blocks_per_seq
  * x block_size / 512) < 4096), where the call may split contexts finer to
- * give every compute unit work. Returns 0 when no workspace is needed
- * (contexts of at most one partition) and for invalid sizes.
+ * give every compute unit work; then one 8-byte exchange word per sequence
+ * and query head (the hand-over of paired rows, below). Returns 0 when no
+ * workspace is needed (contexts of at most one partition) and for invalid
+ * sizes.
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq,
@@ -119,7 +121,10 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  * the per-page attention of the "ATB PagedAttention" page. Long contexts are
  * split into partitions whose partial softmax results are merged exactly
  * (the vLLM-on-CANN page: scattered blocks are merged block by block with an
- * online softmax).
+ * online softmax). When every context fits one workgroup and the batch has
+ * 2 to 64 sequences, rows of unequal length are paired (longest with
+ * shortest) and the longer row's tail is attended by the shorter row's
+ * workgroup; the two partial results are merged the same way, in the call.
  *
  *   out              : [num_seqs, num_q_heads, head_dim], dtype (written)
  *   q                : [num_seqs, num_q_heads, head_dim], dtype
@@ -130,8 +135,13 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   workspace        : device scratch of workspace_bytes bytes, where
  *                      workspace_bytes >= paged_attention_decode_workspace_size(...)
  *                      (may be NULL when that size is 0). Its contents on
- *                      entry do not matter; it is clobbered. Calls that share
- *                      a workspace must be ordered on one stream.
+ *                      entry do not matter; it is clobbered, except that
+ *                      every call leaves the exchange words zero. (Each call
+ *                      tags the words with a number unique to the call, so
+ *                      stale contents are told apart; a replayed graph
+ *                      reuses its number and relies on the words being
+ *                      zero.) Calls that share a workspace must be ordered
+ *                      on one stream.
  * Accepts dtype PKV_F32, PKV_F16, PKV_BF16. Accumulation is fp32.
  */
 int paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -192,7 +202,8 @@ int paged_kv_write_decode(void* out, const void* q, void* k_cache, void* v_cache
  *
  * Every call on one GPU shares that GPU's array, which keeps the last
  * call's partials (each call writes every partial it reads, so nothing
- * needs clearing). Calls that may overlap on one GPU -- on different
+ * needs clearing) and its exchange words, zero at load and left zero by
+ * every call. Calls that may overlap on one GPU -- on different
  * streams, or from different host threads without ordering -- race on it
  * and must be serialised by the caller.
  */

@@ -6,6 +6,7 @@
 
 #include <limits.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "pagedkv.h"
@@ -58,6 +59,28 @@ int decode_num_parts(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
   const bool fine = pkv::decode_fine_ok(num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   return pkv::decode_parts(max_blocks_per_seq, block_size,
                            fine ? pkv::kDecodeFinePart : pkv::kDecodePart);
+}
+
+// Epoch of a decode call that may pair rows: unique per call within the
+// process, never 0 (the value a paired row's word holds between calls).
+unsigned long long next_pair_epoch() {
+  static std::atomic<unsigned long long> counter{0};
+  return counter.fetch_add(1, std::memory_order_relaxed) + 1;
+}
+
+// Points the decode arguments at the workspace: [B, Hq, P, 2] (max, sum),
+// [B, Hq, P, D] partial outputs, P = the finest split, then (when P >= 2)
+// [B, Hq] 64-bit exchange words for paired rows, which use two slots per
+// (sequence, head) of the partials.
+void set_decode_workspace(pkv::DecodeArgs& a, void* workspace, int32_t max_blocks_per_seq) {
+  const int parts = decode_num_parts(a.num_seqs, a.num_q_heads, max_blocks_per_seq, a.block_size);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads * parts;
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  if (workspace && parts >= 2) {
+    a.pair_words = reinterpret_cast<unsigned long long*>(a.ws_o + rows * a.head_dim);
+    a.epoch = next_pair_epoch();
+  }
 }
 
 }  // namespace
@@ -148,10 +171,7 @@ static int write_decode_impl(void* out, const void* q, void* k_cache, void* v_ca
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  set_decode_workspace(a, workspace, max_blocks_per_seq);
   a.app_k_cache = k_cache;
   a.app_v_cache = v_cache;
   a.new_key = key;
@@ -282,8 +302,9 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-// Workspace layout: [B, Hq, P, 2] fp32 (max, sum), then [B, Hq, P, D] fp32
-// partial outputs, P = partitions at the finest split.
+// Workspace layout (set_decode_workspace): [B, Hq, P, 2] fp32 (max, sum),
+// [B, Hq, P, D] fp32 partial outputs, P = partitions at the finest split,
+// then [B, Hq] 64-bit exchange words of paired rows.
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq,
                                              int32_t block_size) {
@@ -292,7 +313,8 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
   const int64_t parts = decode_num_parts(num_seqs, num_q_heads, max_blocks_per_seq, block_size);
   if (parts <= 1) return 0;
   const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
-  return (size_t)(rows * 2 + rows * head_dim) * sizeof(float);
+  return (size_t)(rows * 2 + rows * head_dim) * sizeof(float) +
+         (size_t)num_seqs * num_q_heads * sizeof(unsigned long long);
 }
 
 int paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -330,11 +352,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_cache, const 
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  // partials are laid out for the finest split; a coarser launch plan uses a prefix
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  set_decode_workspace(a, workspace, max_blocks_per_seq);
   hipError_t err = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -455,10 +473,7 @@ int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, con
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  set_decode_workspace(a, workspace, max_blocks_per_seq);
   a.alibi = alibi_slopes;
   a.window_left = window_left < 0 ? -1 : window_left;
   hipError_t err = pkv::launch_decode_ext(a, static_cast<hipStream_t>(stream));
@@ -524,10 +539,7 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  set_decode_workspace(a, workspace, max_blocks_per_seq);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   hipError_t err = pkv::launch_decode_int8(a, static_cast<hipStream_t>(stream));
@@ -573,10 +585,7 @@ int paged_kv_write_decode_int8(void* out, const void* q, void* k_cache, void* v_
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.dtype = dtype;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * decode_num_parts(
-      num_seqs, num_q_heads, max_blocks_per_seq, block_size);
-  a.ws_ml = static_cast<float*>(workspace);
-  a.ws_o = workspace ? a.ws_ml + rows * 2 : nullptr;
+  set_decode_workspace(a, workspace, max_blocks_per_seq);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.app_k_cache = k_cache;

@@ -157,6 +157,11 @@ struct DecodeArgs {
   const void* new_key = nullptr;
   const void* new_value = nullptr;
   const int32_t* slot_mapping = nullptr;
+  // pairing of whole-context rows (NULL: off): one exchange word per
+  // (sequence, query head) in the workspace, and the call's epoch (unique
+  // per call, never 0)
+  unsigned long long* pair_words = nullptr;
+  unsigned long long epoch = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

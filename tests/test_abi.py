@@ -179,13 +179,14 @@ def test_write_decode_int8_validation(L):
 def test_decode_workspace_size(L):
     # one 512-token partition of a large problem -> no workspace
     assert L.paged_attention_decode_workspace_size(64, 64, 128, 512 // 16, 16) == 0
-    # a small problem counts 128-token partitions: 8 x 32 x 4 triples
+    # a small problem counts 128-token partitions: 8 x 32 x 4 triples, then
+    # one 8-byte exchange word per (sequence, head) for paired rows
     assert L.paged_attention_decode_workspace_size(8, 32, 128, 512 // 16, 16) == \
-        8 * 32 * 4 * (2 + 128) * 4
+        8 * 32 * 4 * (2 + 128) * 4 + 8 * 32 * 8
     assert L.paged_attention_decode_workspace_size(1, 8, 128, 128 // 16, 16) == 0
     # 131072-token contexts with bs 128: 256 partitions of (max, sum) + D floats
     got = L.paged_attention_decode_workspace_size(4, 64, 128, 1024, 128)
-    assert got == 4 * 64 * 256 * (2 + 128) * 4
+    assert got == 4 * 64 * 256 * (2 + 128) * 4 + 4 * 64 * 8
     assert L.paged_attention_decode_workspace_size(0, 64, 128, 1024, 128) == 0
     assert L.paged_attention_decode_workspace_size(4, 64, 96, 1024, 128) == 0
 
