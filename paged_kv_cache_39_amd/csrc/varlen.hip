@@ -25,6 +25,11 @@
 namespace pkv {
 
 constexpr int kVlWaves = 4;
+// compile-time stage index of the prefill key loop
+template <int V>
+struct stage_tag {
+  static constexpr int value = V;
+};
 constexpr int kVlThreads = kVlWaves * kWave;
 
 // K / V tiles live in LDS unpadded (D*2-byte rows) and XOR-swizzled in
@@ -505,15 +510,27 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int vrow = 4 * g4 + (l16 >> 2);
   const int vbyte = 8 * (l16 & 1);
   const int vchunk = (l16 & 3) >> 1;
+  // Their lane parts do not depend on the stage or the half: the swizzle
+  // function sees a row only modulo 16 (8 at D = 64), and rows 32hh + 16n +
+  // l16 (K) or 32hh + vrow (+16) (V^T) agree with l16 / vrow there. So a
+  // lane keeps KS + ND byte offsets, and the stage, the half and the row
+  // block are immediate offsets of the LDS reads.
+  uint32_t kofs[KS], vofs[ND];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kofs[s] = l16 * L::rowB + L::slot_k(l16, 4 * s + g4) * 16;
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+    vofs[nd] = L::tileB + vrow * L::rowB + L::slot_v(vrow, 2 * nd + vchunk) * 16 + vbyte;
 
   // A wave whose rows are all padding (a tile of a few queries, such as the
   // decode rows of a mixed batch) only helps stage the tiles and skips the
   // arithmetic.
   const bool wave_live = __builtin_amdgcn_ballot_w64(row_ok[0] || row_ok[1]) != 0;
 
-  int it = 0;
-  for (int kv0 = kv_lo; kv0 < kv_hi; kv0 += kVlBN, ++it) {
-    const int cur = it & 1;
+  // One 64-key tile; CUR, the stage it reads, is a compile-time constant in
+  // each of the two copies the loop below inlines.
+  auto key_tile = [&](auto cur_tag, int kv0, int it) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_tag)::value;
     const bool more = kv0 + kVlBN < kv_hi;
     // this tile's copies (issued one iteration earlier) have landed in LDS,
     // and every wave is past the previous iteration, so the other stage,
@@ -521,8 +538,12 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     wait_vmcnt<0>();
     barrier_lds_ops();
     if (more) stage(cur ^ 1, kv0 + kVlBN);
-    const uint8_t* sk = s_kv + cur * L::stageB;
-    const uint8_t* sv = sk + L::tileB;
+    const uint8_t* sk = s_kv + cur * L::stageB;   // this stage; V^T at sk + tileB
+    // (kept in registers: not hoisted as per-stage sums)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kofs[s]));
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) asm volatile("" : "+v"(vofs[nd]));
     const bool need_mask = kv0 + kVlBN > nomask_end || (windowed && kv0 < mask_lo_end);
     if (wave_live) {
       // Operand reads from LDS are issued a phase ahead of the MFMAs that use
@@ -532,10 +553,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       auto read_k = [&](int hh, u32x4_t (&ka)[2][KS]) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          const int r = 32 * hh + 16 * n + l16;
 #pragma unroll
           for (int s = 0; s < KS; ++s)
-            ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + r * L::rowB + L::slot_k(r, 4 * s + g4) * 16);
+            ka[n][s] = *reinterpret_cast<const u32x4_t*>(sk + kofs[s] + (32 * hh + 16 * n) * L::rowB);
         }
       };
       auto qk = [&](const u32x4_t (&ka)[2][KS], f32x4_t (&st)[2][2]) {
@@ -551,12 +571,10 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         }
       };
       auto read_v = [&](int hh, u32x4_t (&va)[ND]) {
-        const int r0 = 32 * hh + vrow, r1 = r0 + 16;
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
-          const int c = 2 * nd + vchunk;
-          const u32x2_t lo = lds_read_tr16(sv + r0 * L::rowB + L::slot_v(r0, c) * 16 + vbyte);
-          const u32x2_t hi = lds_read_tr16(sv + r1 * L::rowB + L::slot_v(r1, c) * 16 + vbyte);
+          const u32x2_t lo = lds_read_tr16(sk + vofs[nd] + 32 * hh * L::rowB);
+          const u32x2_t hi = lds_read_tr16(sk + vofs[nd] + (32 * hh + 16) * L::rowB);
           va[nd] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
       };
@@ -667,6 +685,10 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
         }
       }
     }
+  };
+  for (int kv0 = kv_lo, it = 0; kv0 < kv_hi; kv0 += 2 * kVlBN, it += 2) {
+    key_tile(stage_tag<0>{}, kv0, it);
+    if (kv0 + kVlBN < kv_hi) key_tile(stage_tag<1>{}, kv0 + kVlBN, it + 1);
   }
 
   if (SPLIT && n_chunks > 1) {
