@@ -418,6 +418,38 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
 const char* pkv_status_string(int status);
 
 /*
+ * Device-side contract reports (the debug build, libpagedkv_debug.so)
+ * -------------------------------------------------------------------
+ * Block ids, lengths, cu_seqlens_q and slots are read on the device, so the
+ * host cannot validate them; the cann-recipes-infer page's fault table
+ * (§5.1) traces crashes to a block_table or cu_seqlens of the wrong dtype or
+ * shape. The kernels keep such values inside the buffers (see the contract
+ * at the top) and say nothing. A build compiled with PKV_DEBUG_CHECKS=1 also
+ * records, as bits of a per-device word, which kinds of violation its
+ * kernels met; the default build compiles the reports out:
+ */
+#define PKV_DBG_BLOCK_ID 1u   /* a used block's id outside [0, num_blocks); a block is used
+                                 when it holds keys below the length and, under a window,
+                                 not only keys before the window */
+#define PKV_DBG_LENGTH 2u     /* a context / KV length < 0 or > max_blocks_per_seq * block_size */
+#define PKV_DBG_CU_SEQLENS 4u /* cu_seqlens_q not non-decreasing from 0 to total_q */
+#define PKV_DBG_SLOT 8u       /* a slot >= num_blocks * block_size (negative slots are skips) */
+#define PKV_DBG_COPY_PAIR 16u /* a paged_kv_copy_blocks pair naming a block outside the pool */
+
+/* 1 when this library was built with PKV_DEBUG_CHECKS=1, else 0. */
+int pkv_debug_checks(void);
+
+/*
+ * pkv_debug_take_errors -- waits for the current device (hipDeviceSynchronize),
+ * stores in *bits the OR of the PKV_DBG_* bits that this library's kernels
+ * reported on that device since the last take, and clears them. Returns
+ * PKV_OK; PKV_ERR_NULL for a NULL bits; PKV_ERR_UNSUPPORTED (and *bits = 0)
+ * in a build without the checks, which touches no device; PKV_ERR_HIP when
+ * the runtime fails.
+ */
+int pkv_debug_take_errors(uint32_t* bits);
+
+/*
  * Tokens per context partition that paged_attention_decode uses for these
  * sizes (informative; 0 for invalid sizes). Contexts longer than one
  * partition are split, and the partial softmax results of the pieces are

@@ -2,12 +2,20 @@
 
     python -m paged_kv_cache_39_amd.build              # build (always recompiles)
     python -m paged_kv_cache_39_amd.build --sanitize   # host-side ASan + UBSan build
+    python -m paged_kv_cache_39_amd.build --debug      # device contract reports
+    python -m paged_kv_cache_39_amd.build --all        # regular + debug, in parallel
 
 The sanitizer build (libpagedkv_sanitize.so) instruments the host code only
 (argument validation, workspace layout, the block manager); its device code
 is the regular build's. It is for CPU test runs: load it through the
 PAGEDKV_LIBRARY environment variable with clang's ASan runtime preloaded
 (see sanitizer_env()).
+
+The debug build (libpagedkv_debug.so) compiles the kernels with
+PKV_DEBUG_CHECKS=1: where a kernel clamps a block id, length, cu_seqlens
+entry, slot or copy pair that breaks the caller's contract, it also records
+the kind in a device word (pkv_debug_take_errors reads it). Same arguments
+and results as the regular build; slower only where it reports.
 """
 
 from __future__ import annotations
@@ -22,6 +30,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SANITIZE_LIB = os.path.join(PKG, "libpagedkv_sanitize.so")
+DEBUG_LIB = os.path.join(PKG, "libpagedkv_debug.so")
 SOURCES = ["api.hip", "kv_write.hip", "decode.hip", "varlen.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
@@ -75,26 +84,56 @@ def sanitizer_env() -> dict:
     return env
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
-    """Compile every source into libpagedkv.so, or with `sanitize` into the
-    host-instrumented libpagedkv_sanitize.so (always recompiles)."""
-    lib = SANITIZE_LIB if sanitize else LIB
-    out_tmp = lib + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *(SANITIZE_FLAGS if sanitize else []), "-shared", "-o",
-           out_tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _command(lib: str, sanitize: bool, debug: bool) -> list[str]:
+    return [hipcc(), *compile_flags(), *(SANITIZE_FLAGS if sanitize else []),
+            *(["-DPKV_DEBUG_CHECKS=1"] if debug else []), "-shared", "-o", lib + ".tmp",
+            *[os.path.join(CSRC, s) for s in SOURCES]]
+
+
+def _finish(lib: str, res_code: int, out: str, verbose: bool) -> str:
     # hipcc's host pass warns that it does not know the packed-fp32 feature
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    msgs = [ln for ln in out.splitlines() if noise not in ln]
+    if res_code != 0:
+        raise RuntimeError(f"hipcc failed for {os.path.basename(lib)}:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(out_tmp, lib)
+    os.replace(lib + ".tmp", lib)
     return lib
 
 
+def build(verbose: bool = False, sanitize: bool = False, debug: bool = False) -> str:
+    """Compile every source into libpagedkv.so, or with `sanitize` into the
+    host-instrumented libpagedkv_sanitize.so, or with `debug` into
+    libpagedkv_debug.so (always recompiles)."""
+    lib = SANITIZE_LIB if sanitize else DEBUG_LIB if debug else LIB
+    cmd = _command(lib, sanitize, debug)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return _finish(lib, res.returncode, res.stdout + res.stderr, verbose)
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """The regular and the debug build, compiled side by side."""
+    jobs = []
+    for lib, debug in ((LIB, False), (DEBUG_LIB, True)):
+        cmd = _command(lib, False, debug)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((lib, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                           stderr=subprocess.STDOUT, text=True)))
+    done = []
+    for lib, proc in jobs:
+        out, _ = proc.communicate()
+        done.append((lib, proc.returncode, out))
+    return [_finish(lib, code, out, verbose) for lib, code, out in done]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv, sanitize="--sanitize" in sys.argv))
+    quiet = "-q" in sys.argv
+    if "--all" in sys.argv:
+        print("\n".join(build_all(verbose=not quiet)))
+    else:
+        print(build(verbose=not quiet, sanitize="--sanitize" in sys.argv,
+                    debug="--debug" in sys.argv))

@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "pagedkv.h"
+#include "debug_checks.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -265,6 +266,23 @@ const char* pkv_status_string(int status) {
       return "the split-KV partials need more than the no-allocation call's scratch";
     default: return "unknown status";
   }
+}
+
+int pkv_debug_checks(void) { return pkv::kDbgBuild ? 1 : 0; }
+
+int pkv_debug_take_errors(uint32_t* bits) {
+  if (!bits) return PKV_ERR_NULL;
+  *bits = 0;
+  if (!pkv::kDbgBuild) return PKV_ERR_UNSUPPORTED;
+  if (hipDeviceSynchronize() != hipSuccess) return PKV_ERR_HIP;
+  uint32_t all = 0;
+  for (auto take : {pkv::debug_take_kv_write, pkv::debug_take_decode, pkv::debug_take_varlen}) {
+    uint32_t b = 0;
+    if (take(&b) != hipSuccess) return PKV_ERR_HIP;
+    all |= b;
+  }
+  *bits = all;
+  return PKV_OK;
 }
 
 int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -23,6 +23,7 @@
 // and the 4 waves are merged once at the end. The partition's block ids are
 // staged in LDS once per workgroup and broadcast to scalar registers.
 
+#include "debug_checks.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
   const int bs = 1 << log2_bs;
 
   int ctx = context_lens[b];
+  PKV_DBG_REPORT(tid == 0 && (ctx < 0 || ctx > (max_blocks_per_seq << log2_bs)), kDbgLength);
   ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
   const int part_start = p * kDecodePart;
   if (part_start >= ctx) {
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
   const int nblk = (ntok + bs - 1) >> log2_bs;
   if (tid < nblk) {
     const int id = block_table[(size_t)b * max_blocks_per_seq + (part_start >> log2_bs) + tid];
+    PKV_DBG_REPORT(!(id >= 0 && id < num_blocks), kDbgBlockId);
     s_blk[tid] = (id >= 0 && id < num_blocks) ? id : -1;
   }
 
@@ -374,8 +377,10 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
     }
 
     int ctx = context_lens[sb];
+    PKV_DBG_REPORT(tid == 0 && (ctx < 0 || ctx > (max_blocks_per_seq << log2_bs)), kDbgLength);
     ctx = max(0, min(ctx, max_blocks_per_seq << log2_bs));
     const int app_slot = APP ? slot_mapping[sb] : -1;
+    PKV_DBG_REPORT(APP && tid == 0 && (int64_t)app_slot >= (num_blocks << log2_bs), kDbgSlot);
     // the item's pair slot (0 head, 1 tail), or -1 for a whole partition
     // (item 0 learns whether it is cut only once its first loads are out)
     int pslot = is_tail ? 1 : -1;
@@ -476,6 +481,9 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
 
     const int nblk = (ntok + bs - 1) >> log2_bs;
     if (tid < nblk) s_blk[tid] = (id_raw >= 0 && id_raw < num_blocks) ? id_raw : -1;
+    // (blocks wholly before a window's first loaded token are never read)
+    PKV_DBG_REPORT(tid < nblk && ((tid + 1) << log2_bs) > tb && !(id_raw >= 0 && id_raw < num_blocks),
+                   kDbgBlockId);
     // APP: wave 0 takes the last tile (the one holding ctx-1) first and the
     // counter hands out the others, so only that first step differs
     if (tid == 0) s_claim = APP ? WAVES - 1 : WAVES;
@@ -1020,5 +1028,7 @@ hipError_t launch_write_decode(const DecodeArgs& a, hipStream_t stream) {
                         : launch_decode_mfma<BF16, 128, false, false, true>(a, stream);
   }
 }
+
+PKV_DBG_TAKE_FN(debug_take_decode)
 
 }  // namespace pkv

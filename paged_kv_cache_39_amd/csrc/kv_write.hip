@@ -9,6 +9,7 @@
 // of a row, so both the read of key/value and the write into the pool are
 // fully coalesced.
 
+#include "debug_checks.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -29,7 +30,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(uint4* __restrict__ k_cac
   const uint4 kk = key[gid];
   const uint4 vv = value[gid];
   const int32_t slot = slot_mapping[t];
-  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  if (slot < 0 || (int64_t)slot >= num_slots) {
+    PKV_DBG_REPORT(slot >= 0 && piece == 0, kDbgSlot);   // (a negative slot is a skip)
+    return;
+  }
   const int64_t dst = (int64_t)slot * pieces_per_row + piece;
   k_cache[dst] = kk;
   v_cache[dst] = vv;
@@ -65,7 +69,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   const int64_t i = gid / pieces_per_block;
   const int piece = (int)(gid - i * pieces_per_block);
   const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+    PKV_DBG_REPORT(piece == 0, kDbgCopyPair);
+    return;
+  }
   const int64_t s = (int64_t)src * pieces_per_block + piece;
   const int64_t d = (int64_t)dst * pieces_per_block + piece;
   const uint4 kk = k_cache[s];
@@ -110,7 +117,10 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(
   const uint4 kq = quantize16<Ty>(key + gid * 16, k_scale[head]);
   const uint4 vq = quantize16<Ty>(value + gid * 16, v_scale[head]);
   const int32_t slot = slot_mapping[t];
-  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  if (slot < 0 || (int64_t)slot >= num_slots) {
+    PKV_DBG_REPORT(slot >= 0 && piece == 0, kDbgSlot);
+    return;
+  }
   const int64_t dst = (int64_t)slot * pieces_per_row + piece;
   k_cache[dst] = kq;
   v_cache[dst] = vq;
@@ -145,5 +155,7 @@ hipError_t launch_kv_write_int8(void* k_cache, void* v_cache, const void* key, c
   }
   return hipGetLastError();
 }
+
+PKV_DBG_TAKE_FN(debug_take_kv_write)
 
 }  // namespace pkv

@@ -234,4 +234,10 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream);
 hipError_t launch_varlen_ext(const VarlenArgs& a, hipStream_t stream);
 hipError_t launch_varlen_split(const VarlenArgs& a, hipStream_t stream);
 
+// the debug build's per-source report words (debug_checks.h) on the current
+// device, read and cleared; the default build returns 0 bits
+hipError_t debug_take_kv_write(uint32_t* bits);
+hipError_t debug_take_decode(uint32_t* bits);
+hipError_t debug_take_varlen(uint32_t* bits);
+
 }  // namespace pkv

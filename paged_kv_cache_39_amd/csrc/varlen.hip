@@ -20,6 +20,7 @@
 // lane's registers, with only two cross-lane exchanges per row for the max.
 // V is transposed once while it is staged into LDS.
 
+#include "debug_checks.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -276,6 +277,17 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   const int bq = kVlRows / group;   // query positions per tile
   const int bq_log2 = (bq & (bq - 1)) == 0 ? __builtin_ctz(bq) : -1;
   const int bs = 1 << log2_bs;
+  if constexpr (kDbgBuild) {   // the batch's metadata, checked once (workgroup 0)
+    if (blockIdx.x == 0 && tid < kWave) {
+      for (int s = lane; s < num_seqs; s += kWave) {
+        const int c0 = cu_seqlens_q[s], c1 = cu_seqlens_q[s + 1], kl = seq_lens[s];
+        PKV_DBG_REPORT(c0 < 0 || c1 < c0 || c1 > total_q || (s == 0 && c0 != 0) ||
+                           (s == num_seqs - 1 && c1 != total_q),
+                       kDbgCuSeqlens);
+        PKV_DBG_REPORT(kl < 0 || kl > (max_blocks_per_seq << log2_bs), kDbgLength);
+      }
+    }
+  }
 
   // Every wave locates the tile (same inputs, same result: no LDS hand-off
   // and no barrier). Lane s first reads sequence s's metadata (first row,
@@ -414,12 +426,21 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   };
   // byte offset of pool row r (a 32-bit row index) as a signed 64-bit value
   auto row_offset = [&](int r) { return (int64_t)r * (int64_t)row_bytes; };
+  // (debug build) an out-of-range id of a block the tile uses: one holding
+  // keys below Lk and, under a window, not wholly before the first row's
+  auto dbg_block = [&](int raw, int blk_index) {
+    PKV_DBG_REPORT((uint32_t)raw >= nblocks32 && (blk_index << log2_bs) < lk &&
+                       ((blk_index + 1) << log2_bs) > (windowed ? q0 + delta - window_left : 0),
+                   kDbgBlockId);
+  };
   auto stage = [&](int st, int kv0) {
     const uint32_t lds_st = lds_kv + (uint32_t)(st * L::stageB);
     const int i0 = kv0 >> log2_bs;
     if (kv0 + kVlBN <= lk) {
       if (bs >= kVlBN) {   // the whole tile lies in one block: one base
-        const int blk = valid_block(__builtin_amdgcn_readfirstlane(bt_row[i0]));
+        const int raw = __builtin_amdgcn_readfirstlane(bt_row[i0]);
+        dbg_block(raw, i0);
+        const int blk = valid_block(raw);
         const int64_t base = row_offset(blk * bs + (kv0 & (bs - 1)));
         const uint8_t* kb = kbytes + base;
         const uint8_t* vb = vbytes + base;
@@ -443,6 +464,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
           const int rbase = (j * kVlWaves + wave) * RPI;
+          dbg_block(ids[j], i0 + (rbase >> log2_bs));
           const int64_t src = row_offset(valid_block(ids[j]) * bs - (rbase & ~(bs - 1)));
           async_copy16_to_lds(kbytes + src, voffk_[j], lds_st + rbase * L::rowB);
           async_copy16_to_lds(vbytes + src, voffv_[j], lds_st + L::tileB + rbase * L::rowB);
@@ -455,9 +477,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     // cover the copies in flight)
     int ids[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ids[e] = valid_block(
-          __builtin_amdgcn_readfirstlane(bt_row[min(i0 + e, max_blocks_per_seq - 1)]));
+    for (int e = 0; e < 4; ++e) {
+      const int raw = __builtin_amdgcn_readfirstlane(bt_row[min(i0 + e, max_blocks_per_seq - 1)]);
+      dbg_block(raw, i0 + e);
+      ids[e] = valid_block(raw);
+    }
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int rbase = (j * kVlWaves + wave) * RPI;
@@ -839,5 +863,7 @@ hipError_t launch_varlen_split(const VarlenArgs& a, hipStream_t stream) {
     return launch_varlen_any<false, false>(a, stream);
   return launch_varlen_any<false, true>(a, stream);
 }
+
+PKV_DBG_TAKE_FN(debug_take_varlen)
 
 }  // namespace pkv

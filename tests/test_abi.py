@@ -45,6 +45,33 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), f"{name} declared in pagedkv.h but not exported"
 
 
+def test_debug_entry_points_of_the_regular_build(L):
+    """The regular build has no device reports: it says so and touches no
+    device."""
+    bits = ctypes.c_uint32(123)
+    assert L.pkv_debug_checks() == 0
+    assert L.pkv_debug_take_errors(ctypes.byref(bits)) == PKV_ERR_UNSUPPORTED
+    assert bits.value == 0
+    assert L.pkv_debug_take_errors(None) == PKV_ERR_NULL
+
+
+def test_debug_build_exports_and_validates_like_the_regular_build(L):
+    """libpagedkv_debug.so (PKV_DEBUG_CHECKS=1) exports every declared symbol,
+    says it reports, and rejects the same host-side arguments."""
+    if not os.path.exists(binding.DEBUG_LIB_PATH):
+        pytest.skip("libpagedkv_debug.so not built")
+    D = binding.load(binding.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(D, name), f"{name} not exported by the debug build"
+    assert D.pkv_debug_checks() == 1
+    assert D.pkv_debug_take_errors(None) == PKV_ERR_NULL
+    for kw in (dict(dtype=0), dict(hq=6, hkv=4), dict(d=256), dict(cu=None), dict(tq=0, q=None),
+               dict(tq=2**30 - 1, hq=4096, hkv=4096)):
+        assert varlen(D, **kw) == varlen(L, **kw), kw
+    for kw in (dict(n=0, k=None), dict(d=96), dict(bs=24), dict(slots=None)):
+        assert write(D, **kw) == write(L, **kw), kw
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         s = binding.status_string(st)
