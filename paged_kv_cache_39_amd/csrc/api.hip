@@ -208,8 +208,11 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
   // the one-dimensional grid: (query tiles [+ split chunk slots]) x kv heads
   const int64_t splits =
       split ? pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits : 1;
+  // (the plain call also has one workgroup per (sequence, kv head) for the
+  // sequences whose rows fit one 16-row tile)
   const int64_t wgs =
-      pkv::varlen_tiles(total_q, num_seqs, num_q_heads / num_kv_heads) * splits * num_kv_heads;
+      (pkv::varlen_tiles(total_q, num_seqs, num_q_heads / num_kv_heads) * splits +
+       (split || ext ? 0 : num_seqs)) * num_kv_heads;
   if (wgs > INT32_MAX) return PKV_ERR_SHAPE;
   if (split) {
     const size_t need = paged_attention_varlen_workspace_size(

@@ -57,6 +57,203 @@ struct VlLds {
   static __device__ __forceinline__ int slot_v(int r, int chunk) { return chunk ^ fv(r); }
 };
 
+// Narrow sequences of the plain packed call: when all of a sequence's query
+// rows fit one 16-row matrix-core tile (Lq x group <= 16: decode rows,
+// multi-token decode), a 128-row query tile would leave most rows empty and
+// keep one 64-key K/V stage in flight, which bounds a long row's stream (a
+// decode row over 4096 keys took ~1.45 us per 64 keys). Such a sequence is
+// taken per kv head the way the decode kernel takes a context: each wave
+// walks its own 32-key tiles (wave w: tiles w, w + 4, ...), fetched into
+// registers one tile ahead and parked in the wave's own padded LDS slice (no
+// barrier in the loop, four tiles streaming at once), with its own online
+// softmax over the 16 rows; the four partial states merge at the end. Row r
+// of the tile (lane r mod 16) is query r / group, head r mod group of the kv
+// head; query i sees keys j <= i + Lk - Lq under the causal mask.
+template <int D>
+struct VlNarrowLds {
+  static constexpr int TT = 32;                      // keys per wave tile
+  static constexpr int rowB = D * 2 + 16;            // padded row pitch (bytes)
+  static constexpr int tileB = TT * rowB;            // one K or V tile
+  static constexpr int waveB = 2 * tileB;
+  static constexpr int tilesB = kVlWaves * waveB;
+  static constexpr int oRow = D + 4;                 // merge row pitch (floats)
+  static constexpr int mergeB = kVlWaves * 16 * (2 + oRow) * 4;
+  static constexpr int bytes = tilesB > mergeB ? tilesB : mergeB;
+};
+// the most query rows a narrow sequence has
+constexpr int kVlNarrowRows = 16;
+
+template <class Ty, int D>
+__device__ __forceinline__ void varlen_narrow(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const uint8_t* __restrict__ kbytes, const uint8_t* __restrict__ vbytes,
+    const int32_t* __restrict__ bt_row, int r0, int lq, int lk, int causal, int num_q_heads,
+    int kvh, int group, int log2_bs, uint32_t nblocks32, uint32_t row_bytes, float scale_log2,
+    uint8_t* lds, int tid, int wave, int lane) {
+  using N = VlNarrowLds<D>;
+  constexpr int TT = N::TT;
+  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row of one kv head
+  constexpr int RPI = kWave / CPR;    // rows per load instruction
+  constexpr int LPI = TT / RPI;       // load instructions per tile and matrix
+  constexpr int KS = D / 32;          // k-steps of q.k
+  constexpr int ND = D / 16;          // 16-dim tiles of the output
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int lrow = lane / CPR, lch = lane % CPR;
+  const int bs = 1 << log2_bs;
+  // the lane's row of the tile and its last visible key (-1: none)
+  const int qi = l16 / group;
+  const bool row_ok = qi < lq;
+  const int head = kvh * group + (l16 - qi * group);
+  const int lim = row_ok ? (causal ? min(lk - 1, qi + lk - lq) : lk - 1) : -1;
+
+  // queries as the B operand: lane holds row l16, dims 32s + 8*g4 .. +8
+  u32x4_t qb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qb[s] = row_ok ? load16<false>(q + ((size_t)(r0 + qi) * num_q_heads + head) * D + 32 * s +
+                                   8 * g4)
+                   : u32x4_t{0u, 0u, 0u, 0u};
+
+  uint8_t* s_k = lds + wave * N::waveB;
+  uint8_t* s_v = s_k + N::tileB;
+  const int ntiles = (lk + TT - 1) / TT;
+  const uint32_t head_off = (uint32_t)(kvh * D + lch * 8) * 2u;
+  // Block ids of the lane's keys in a tile (keys past Lk re-read key Lk-1:
+  // finite values, masked); the next tile's are requested with the current
+  // tile's K/V, so the fetch never waits on a table lookup.
+  int ids[LPI];
+  auto load_ids = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j)
+      ids[j] = bt_row[min(g * TT + j * RPI + lrow, lk - 1) >> log2_bs];
+  };
+  u32x4_t kr[LPI], vr[LPI];
+  auto fetch = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) {
+      const int t = min(g * TT + j * RPI + lrow, lk - 1);
+      PKV_DBG_REPORT((uint32_t)ids[j] >= nblocks32, kDbgBlockId);
+      const uint32_t blk = (uint32_t)ids[j] < nblocks32 ? (uint32_t)ids[j] : 0u;
+      const size_t off = ((size_t)blk * bs + (t & (bs - 1))) * row_bytes + head_off;
+      kr[j] = load16<true>(kbytes + off);
+      vr[j] = load16<true>(vbytes + off);
+    }
+  };
+  auto park = [&]() {
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) {
+      *reinterpret_cast<u32x4_t*>(s_k + (j * RPI + lrow) * N::rowB + lch * 16) = kr[j];
+      *reinterpret_cast<u32x4_t*>(s_v + (j * RPI + lrow) * N::rowB + lch * 16) = vr[j];
+    }
+  };
+
+  f32x4_t acc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) acc[nd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // V^T operand: lane i of a 16-lane group reads key 4*g4 + i/4 (+16),
+  // dims 16nd + 4*(i%4) .. +4, and receives dim 16nd + i of keys 4*g4 .. +4
+  const uint8_t* vt = s_v + (4 * g4 + (l16 >> 2)) * N::rowB + (l16 & 3) * 8;
+  auto tile = [&](int g) {
+    f32x4_t st[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      st[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(s_k + (16 * n + l16) * N::rowB + 64 * s + 16 * g4);
+        st[n] = Mma<Ty>::mfma(a, qb[s], st[n]);
+      }
+    }
+    // lane holds keys g*TT + 16n + 4*g4 + i of its row
+    const int tbase = g * TT + 4 * g4;
+    float sv[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[n][i] = tbase + 16 * n + i <= lim ? st[n][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[n][i]);
+      }
+    mx = max_xor32(max_xor16(mx));
+    const float mnew = fmaxf(m_run, mx);
+    const float mref = safe_max_ref(mnew);
+    const float alpha = fast_exp2(m_run - mref);
+    m_run = mnew;
+    float pv[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[n][i] = fast_exp2(sv[n][i] - mref);
+        psum += pv[n][i];
+      }
+    l_run = l_run * alpha + psum;
+    const u32x4_t pb = {Mma<Ty>::pack(pv[0][0], pv[0][1]), Mma<Ty>::pack(pv[0][2], pv[0][3]),
+                        Mma<Ty>::pack(pv[1][0], pv[1][1]), Mma<Ty>::pack(pv[1][2], pv[1][3])};
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      const u32x2_t lo = lds_read_tr16(vt + nd * 32);
+      const u32x2_t hi = lds_read_tr16(vt + 16 * N::rowB + nd * 32);
+      const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+      acc[nd] *= alpha;
+      acc[nd] = Mma<Ty>::mfma(a, pb, acc[nd]);
+    }
+  };
+
+  int g = wave;
+  if (g < ntiles) {
+    load_ids(g);
+    fetch(g);
+    if (g + kVlWaves < ntiles) load_ids(g + kVlWaves);
+  }
+  while (g < ntiles) {
+    park();
+    const int gn = g + kVlWaves;
+    if (gn < ntiles) {
+      fetch(gn);
+      if (gn + kVlWaves < ntiles) load_ids(gn + kVlWaves);
+    }
+    tile(g);
+    g = gn;
+  }
+
+  // ---- merge the lane groups, then the waves ----
+  l_run = sum_xor32(sum_xor16(l_run));
+  __syncthreads();   // every wave is done with its tiles
+  float* s_ml = reinterpret_cast<float*>(lds);         // [wave][16][2]
+  float* s_o = s_ml + kVlWaves * 16 * 2;                // [wave][16][oRow]
+  if (g4 == 0) {
+    s_ml[(wave * 16 + l16) * 2 + 0] = m_run;
+    s_ml[(wave * 16 + l16) * 2 + 1] = l_run;
+  }
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+    *reinterpret_cast<f32x4_t*>(s_o + (wave * 16 + l16) * N::oRow + 16 * nd + 4 * g4) = acc[nd];
+  __syncthreads();
+  const int rows = lq * group;
+  for (int idx = tid; idx < rows * D; idx += kVlThreads) {
+    const int r = idx / D, d = idx - r * D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kVlWaves; ++w) mm = fmaxf(mm, s_ml[(w * 16 + r) * 2]);
+    const float mr = safe_max_ref(mm);
+    float ll = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kVlWaves; ++w) {
+      const float wt = fast_exp2(s_ml[(w * 16 + r) * 2] - mr);
+      ll += s_ml[(w * 16 + r) * 2 + 1] * wt;
+      a += s_o[(w * 16 + r) * N::oRow + d] * wt;
+    }
+    const int i = r / group;
+    out[((size_t)(r0 + i) * num_q_heads + kvh * group + (r - i * group)) * D + d] =
+        from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
+  }
+}
+
 // Query-tile count of sequence s (0 past the end).
 __device__ __forceinline__ int seq_tiles(const int32_t* __restrict__ cu, int num_seqs, int bq,
                                          int total_q, int s) {
@@ -155,7 +352,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
                                               const int32_t* __restrict__ seq_lens,
                                               int num_seqs, int total_q, int max_lk, int bq,
                                               int bq_log2, int causal, int g, int lane, int my_lq,
-                                              int my_lk, int& seq, int& q0) {
+                                              int my_lk, int narrow_q, int& seq, int& q0) {
   auto meta = [&](int s0, int& lq, int& lk) {
     if (s0 == 0) {
       lq = my_lq;
@@ -168,6 +365,7 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     if (s < num_seqs) {
       const int r0 = max(0, min(cu[s], total_q));
       lq = max(0, min(cu[s + 1], total_q) - r0);
+      if (lq <= narrow_q) lq = 0;   // taken by the narrow path
       lk = max(0, min(seq_lens[s], max_lk));
     }
   };
@@ -248,7 +446,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     const int32_t* __restrict__ seq_lens, int causal, int num_seqs, int total_q, int num_q_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, float scale_log2,
     const float* __restrict__ alibi, int window_left, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o, int chunk_tiles, int max_splits, int n_tiles) {
+    float* __restrict__ ws_o, int chunk_tiles, int max_splits, int n_tiles, int narrow_seqs) {
   using L = VlLds<D>;
   constexpr int KS = D / 32;                 // k-steps of the QK product
   constexpr int ND = D / 16;                 // 16-wide dim tiles of the output
@@ -257,7 +455,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // lazy rescale: the running max used for the exponentials only moves when
   // a row max exceeds it by more than 2^8 (P then stays <= 256)
   constexpr float kRescale = 8.f;
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * L::stageB];
+  // the plain call's narrow sequences (narrow_seqs > 0) reuse the stages
+  constexpr bool NARROW = !EXT && !SPLIT;
+  constexpr int kLdsB = NARROW && VlNarrowLds<D>::bytes > 2 * L::stageB ? VlNarrowLds<D>::bytes
+                                                                          : 2 * L::stageB;
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[kLdsB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps derived addresses scalar
@@ -267,8 +469,11 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // head's heaviest tiles start first, and when Hkv is a multiple of 8 each
   // XCD serves fixed kv heads, whose K/V then stay in its L2 (with fewer kv
   // heads, a head's tiles alternate over the XCDs).
+  // The plain call puts one workgroup per (narrow sequence candidate, kv
+  // head) first: indexes below narrow_seqs x Hkv (sequences that are not
+  // narrow leave at once); the query tiles follow.
   const int kvh = blockIdx.x % num_kv_heads;
-  const int slot = blockIdx.x / num_kv_heads;
+  const int slot = (int)(blockIdx.x / num_kv_heads) - (NARROW ? narrow_seqs : 0);
   const bool extra = SPLIT && slot >= n_tiles;
   const int tile = slot;
   const int chunk = extra ? 1 + (slot - n_tiles) % (max_splits - 1) : 0;
@@ -288,6 +493,24 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       }
     }
   }
+  // rows of a sequence the narrow path takes (0: none); the tile lookup
+  // below skips those sequences
+  const int narrow_q = NARROW && narrow_seqs > 0 ? kVlNarrowRows / group : 0;   // queries
+  if constexpr (NARROW) {
+    if (slot < 0) {   // uniform: a (sequence, kv head) of the narrow path
+      const int b = (int)(blockIdx.x / num_kv_heads);
+      const int r0 = max(0, min(cu_seqlens_q[b], total_q));
+      const int lq = max(0, min(cu_seqlens_q[b + 1], total_q) - r0);
+      const int lk = max(0, min(seq_lens[b], max_blocks_per_seq << log2_bs));
+      if (lq == 0 || lq > narrow_q) return;
+      varlen_narrow<Ty, D>(out, q, reinterpret_cast<const uint8_t*>(k_cache),
+                           reinterpret_cast<const uint8_t*>(v_cache),
+                           block_table + (size_t)b * max_blocks_per_seq, r0, lq, lk, causal,
+                           num_q_heads, kvh, group, log2_bs, (uint32_t)num_blocks,
+                           (uint32_t)(num_kv_heads * D) * 2u, scale_log2, s_kv, tid, wave, lane);
+      return;
+    }
+  }
 
   // Every wave locates the tile (same inputs, same result: no LDS hand-off
   // and no barrier). Lane s first reads sequence s's metadata (first row,
@@ -299,6 +522,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     if (lane < num_seqs) {
       my_r0 = max(0, min(cu_seqlens_q[lane], total_q));
       my_lq = max(0, min(cu_seqlens_q[lane + 1], total_q) - my_r0);
+      if (my_lq <= narrow_q) my_lq = 0;   // taken by the narrow path
       my_lk = max(0, min(seq_lens[lane], max_blocks_per_seq << log2_bs));
     }
     const int nt0 = my_lq > 0 ? div_bq(my_lq + bq - 1, bq, bq_log2) : 0;
@@ -317,7 +541,7 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
                   ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
                   : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
                                   max_blocks_per_seq << log2_bs, bq, bq_log2, causal, tile, lane,
-                                  my_lq, my_lk, seq, q0);
+                                  my_lq, my_lk, narrow_q, seq, q0);
     }
     if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
@@ -821,7 +1045,9 @@ static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
   const VarlenSplit sp = SPLIT ? plan_varlen_split(a.max_blocks_per_seq, a.block_size)
                                : VarlenSplit{1, 1};
   const int64_t extra = SPLIT ? (int64_t)a.num_seqs * (sp.max_splits - 1) : 0;
-  dim3 grid((unsigned)((tiles + extra) * a.num_kv_heads));
+  // the plain call's narrow-path workgroups: one per (sequence, kv head)
+  const int narrow_seqs = !EXT && !SPLIT ? a.num_seqs : 0;
+  dim3 grid((unsigned)((narrow_seqs + tiles + extra) * a.num_kv_heads));
   launch_kernel((varlen_prefill_kernel<Ty, D, EXT, SPLIT>), grid, dim3(kVlThreads), 0, stream,
                 static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.q),
                 a.cu_seqlens_q, static_cast<const uint16_t*>(a.k_cache),
@@ -829,7 +1055,7 @@ static hipError_t launch_varlen_t(const VarlenArgs& a, hipStream_t stream) {
                 a.num_seqs, (int)a.total_q, a.num_q_heads, a.num_kv_heads,
                 __builtin_ctz(a.block_size), a.max_blocks_per_seq, a.num_blocks, scale_log2,
                 a.alibi, a.window_left, a.ws_ml, a.ws_o, sp.chunk_tiles, sp.max_splits,
-                (int)tiles);
+                (int)tiles, narrow_seqs);
   hipError_t err = hipGetLastError();
   if (!SPLIT || err != hipSuccess) return err;
   launch_kernel((varlen_merge_kernel<Ty, D>), dim3((unsigned)(a.num_seqs * a.num_kv_heads)),
