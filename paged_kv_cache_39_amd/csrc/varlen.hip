@@ -87,8 +87,9 @@ template <class Ty, int D>
 __device__ __forceinline__ void varlen_narrow(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint8_t* __restrict__ kbytes, const uint8_t* __restrict__ vbytes,
-    const int32_t* __restrict__ bt_row, int r0, int lq, int lk, int causal, int num_q_heads,
-    int kvh, int group, int log2_bs, uint32_t nblocks32, uint32_t row_bytes, float scale_log2,
+    const int32_t* __restrict__ bt_row, int r0, int lq, int lk, int kv_lo, int kv_hi, int causal,
+    int num_q_heads, int kvh, int group, int log2_bs, uint32_t nblocks32, uint32_t row_bytes,
+    float scale_log2, float* __restrict__ ws_ml, float* __restrict__ ws_o, int64_t ws_row0,
     uint8_t* lds, int tid, int wave, int lane) {
   using N = VlNarrowLds<D>;
   constexpr int TT = N::TT;
@@ -100,11 +101,12 @@ __device__ __forceinline__ void varlen_narrow(
   const int l16 = lane & 15, g4 = lane >> 4;
   const int lrow = lane / CPR, lch = lane % CPR;
   const int bs = 1 << log2_bs;
-  // the lane's row of the tile and its last visible key (-1: none)
+  // the lane's row of the tile and its last visible key in [kv_lo, kv_hi)
+  // (below kv_lo: none)
   const int qi = l16 / group;
   const bool row_ok = qi < lq;
   const int head = kvh * group + (l16 - qi * group);
-  const int lim = row_ok ? (causal ? min(lk - 1, qi + lk - lq) : lk - 1) : -1;
+  const int lim = row_ok ? (causal ? min(kv_hi - 1, qi + lk - lq) : kv_hi - 1) : kv_lo - 1;
 
   // queries as the B operand: lane holds row l16, dims 32s + 8*g4 .. +8
   u32x4_t qb[KS];
@@ -116,22 +118,22 @@ __device__ __forceinline__ void varlen_narrow(
 
   uint8_t* s_k = lds + wave * N::waveB;
   uint8_t* s_v = s_k + N::tileB;
-  const int ntiles = (lk + TT - 1) / TT;
+  const int ntiles = (kv_hi - kv_lo + TT - 1) / TT;
   const uint32_t head_off = (uint32_t)(kvh * D + lch * 8) * 2u;
-  // Block ids of the lane's keys in a tile (keys past Lk re-read key Lk-1:
-  // finite values, masked); the next tile's are requested with the current
-  // tile's K/V, so the fetch never waits on a table lookup.
+  // Block ids of the lane's keys in a tile (keys past the range re-read its
+  // last key: finite values, masked); the next tile's are requested with the
+  // current tile's K/V, so the fetch never waits on a table lookup.
   int ids[LPI];
   auto load_ids = [&](int g) {
 #pragma unroll
     for (int j = 0; j < LPI; ++j)
-      ids[j] = bt_row[min(g * TT + j * RPI + lrow, lk - 1) >> log2_bs];
+      ids[j] = bt_row[min(kv_lo + g * TT + j * RPI + lrow, kv_hi - 1) >> log2_bs];
   };
   u32x4_t kr[LPI], vr[LPI];
   auto fetch = [&](int g) {
 #pragma unroll
     for (int j = 0; j < LPI; ++j) {
-      const int t = min(g * TT + j * RPI + lrow, lk - 1);
+      const int t = min(kv_lo + g * TT + j * RPI + lrow, kv_hi - 1);
       PKV_DBG_REPORT((uint32_t)ids[j] >= nblocks32, kDbgBlockId);
       const uint32_t blk = (uint32_t)ids[j] < nblocks32 ? (uint32_t)ids[j] : 0u;
       const size_t off = ((size_t)blk * bs + (t & (bs - 1))) * row_bytes + head_off;
@@ -166,8 +168,8 @@ __device__ __forceinline__ void varlen_narrow(
         st[n] = Mma<Ty>::mfma(a, qb[s], st[n]);
       }
     }
-    // lane holds keys g*TT + 16n + 4*g4 + i of its row
-    const int tbase = g * TT + 4 * g4;
+    // lane holds keys kv_lo + g*TT + 16n + 4*g4 + i of its row
+    const int tbase = kv_lo + g * TT + 4 * g4;
     float sv[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -248,9 +250,20 @@ __device__ __forceinline__ void varlen_narrow(
       ll += s_ml[(w * 16 + r) * 2 + 1] * wt;
       a += s_o[(w * 16 + r) * N::oRow + d] * wt;
     }
-    const int i = r / group;
-    out[((size_t)(r0 + i) * num_q_heads + kvh * group + (r - i * group)) * D + d] =
-        from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
+    if (ws_row0 >= 0) {
+      // a chunk of a cut sequence: (max, sum, output) relative to 2^max for
+      // the merge kernel, row r at slot ws_row0 + r
+      const int64_t slot_i = ws_row0 + r;
+      ws_o[slot_i * D + d] = a;
+      if (d == 0) {
+        ws_ml[slot_i * 2 + 0] = mm;
+        ws_ml[slot_i * 2 + 1] = ll;
+      }
+    } else {
+      const int i = r / group;
+      out[((size_t)(r0 + i) * num_q_heads + kvh * group + (r - i * group)) * D + d] =
+          from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
+    }
   }
 }
 
@@ -457,8 +470,9 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   constexpr float kRescale = 8.f;
   // the plain call's narrow sequences (narrow_seqs > 0) reuse the stages
   constexpr bool NARROW = !EXT && !SPLIT;
-  constexpr int kLdsB = NARROW && VlNarrowLds<D>::bytes > 2 * L::stageB ? VlNarrowLds<D>::bytes
-                                                                          : 2 * L::stageB;
+  // (the split call's chunks of narrow sequences take the narrow path too)
+  constexpr int kLdsB = !EXT && VlNarrowLds<D>::bytes > 2 * L::stageB ? VlNarrowLds<D>::bytes
+                                                                        : 2 * L::stageB;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[kLdsB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -505,9 +519,10 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       if (lq == 0 || lq > narrow_q) return;
       varlen_narrow<Ty, D>(out, q, reinterpret_cast<const uint8_t*>(k_cache),
                            reinterpret_cast<const uint8_t*>(v_cache),
-                           block_table + (size_t)b * max_blocks_per_seq, r0, lq, lk, causal,
-                           num_q_heads, kvh, group, log2_bs, (uint32_t)num_blocks,
-                           (uint32_t)(num_kv_heads * D) * 2u, scale_log2, s_kv, tid, wave, lane);
+                           block_table + (size_t)b * max_blocks_per_seq, r0, lq, lk, 0, lk,
+                           causal, num_q_heads, kvh, group, log2_bs, (uint32_t)num_blocks,
+                           (uint32_t)(num_kv_heads * D) * 2u, scale_log2, nullptr, nullptr, -1,
+                           s_kv, tid, wave, lane);
       return;
     }
   }
@@ -610,6 +625,20 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     if (n_chunks > 1) {              // a tile that is not cut keeps its whole loop
       kv_lo = kv_begin + chunk * chunk_tiles * kVlBN;
       kv_hi = min(kv_end, kv_lo + chunk_tiles * kVlBN);
+    }
+    // a narrow sequence (one tile of at most 16 rows): its whole tile or
+    // this chunk of it through the narrow path, the chunk's triple into the
+    // same slots as below
+    if (lq <= kVlNarrowRows / group) {   // uniform
+      const int64_t ws_row0 =
+          n_chunks > 1 ? (((int64_t)chunk * num_seqs + b) * num_kv_heads + kvh) * kVlRowsWave : -1;
+      varlen_narrow<Ty, D>(out, q, reinterpret_cast<const uint8_t*>(k_cache),
+                           reinterpret_cast<const uint8_t*>(v_cache),
+                           block_table + (size_t)b * max_blocks_per_seq, row0, lq, lk, kv_lo,
+                           kv_hi, causal, num_q_heads, kvh, group, log2_bs, (uint32_t)num_blocks,
+                           (uint32_t)(num_kv_heads * D) * 2u, scale_log2, ws_ml, ws_o, ws_row0,
+                           s_kv, tid, wave, lane);
+      return;
     }
   }
   const int mask_lo_end = windowed ? max(0, last_q + delta - window_left) : 0;
