@@ -42,6 +42,11 @@ struct item_kind {
 // shortest tail a paired row hands over (a second item costs its workgroup
 // about one more round trip to memory)
 constexpr int kPairMinTail = 256;
+// K/V bytes by which the longer row's piece exceeds the shorter row's
+// workgroup's share: that workgroup also pays a second item's start (table,
+// queries, first tile) and the hand-over, ~3-4 us of streaming (measured
+// best among 64, 96, 128 and 160 KB on the ragged GQA batch)
+constexpr int kPairBiasBytes = 96 * 1024;
 
 template <class Ty, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_partition_kernel(
@@ -338,7 +343,8 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
   // at most 64 sequences). The sequences are ranked by context length,
   // longest first (ties by index), and rank k is paired with rank B-1-k.
   // When the longer context exceeds the split point -- the middle of the
-  // two lengths, rounded down to a multiple of the tile and the block -- by
+  // two lengths moved toward the longer row by half of kPairBiasBytes,
+  // rounded down to a multiple of the tile and the block -- by
   // at least kPairMinTail tokens, the longer row's workgroup stops there and
   // the shorter row's workgroup attends the rest after its own row. The two
   // partial triples meet in the workspace; the workgroup that finishes
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(WAVES * kWave) void decode_mfma_kernel(
       }
       const int lb = kb >> 6, lp = k >> 6;
       const int quant = max(TT, bs);
-      const int at = ((min(lb, lp) + max(lb, lp)) >> 1) & ~(quant - 1);
+      const int at = ((lb + lp + kPairBiasBytes / (2 * D * EB)) >> 1) & ~(quant - 1);
       // (a head piece keeps at least the first tile of every wave)
       if (max(lb, lp) - at < kPairMinTail || at < WAVES * TT) return;
       if (rb < rp) {
