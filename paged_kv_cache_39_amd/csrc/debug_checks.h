@@ -57,8 +57,10 @@ static __device__ uint32_t pkv_dbg_word;
     return e;                                                                        \
   }
 #else
+// (the condition is named, unevaluated, so that its operands count as used)
 #define PKV_DBG_REPORT(cond, bit) \
   do {                            \
+    (void)sizeof((cond) && (bit)); \
   } while (0)
 #define PKV_DBG_TAKE_FN(name)       \
   hipError_t name(uint32_t* bits) { \
