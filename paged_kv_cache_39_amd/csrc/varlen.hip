@@ -330,28 +330,32 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ cu, int nu
   return false;
 }
 
+// x / bq for x >= 0: a shift when bq is a power of two (P2, bq_log2 >= 0:
+// the usual group sizes), else a division. The lookup below is compiled
+// once per case and picked by a uniform branch: with a select per use, the
+// compiler runs the division's ~25 instructions beside the shift every time.
+template <bool P2>
+__device__ __forceinline__ int div_bq(int x, int bq, int bq_log2) {
+  return P2 ? (x >> bq_log2) : x / bq;
+}
+
 // Key tiles (of kVlBN keys) that a query tile's loop runs over: up to its
 // rows' highest visible key, i + Lk - Lq for the tile's last row i under the
 // causal mask, else Lk. That bound grows with the tile's position, so the
 // tiles of a sequence needing at least w key tiles form a suffix; this
-// returns its length (lq, lk: the sequence's query and key counts).
-// x / bq for x >= 0: a shift when bq is a power of two (bq_log2 >= 0, the
-// usual group sizes), else a division
-__device__ __forceinline__ int div_bq(int x, int bq, int bq_log2) {
-  return bq_log2 >= 0 ? (x >> bq_log2) : x / bq;
-}
-
-__device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, int bq_log2,
+// returns its length (nt, lq, lk: the sequence's query tiles, query and key
+// counts).
+template <bool P2>
+__device__ __forceinline__ int tiles_with_work(int w, int nt, int lq, int lk, int bq, int bq_log2,
                                                int causal) {
   if (lq <= 0) return 0;
-  const int nt = div_bq(lq + bq - 1, bq, bq_log2);
   if (w <= 0) return nt;
   const int kmin = (w - 1) * kVlBN;   // the loop end must exceed this
   if (lk <= kmin) return 0;
   if (!causal) return nt;
   const int x = kmin - (lk - lq);      // needs min((t + 1) * bq, lq) > x
   if (lq <= x) return 0;
-  return x < 0 ? nt : nt - div_bq(x, bq, bq_log2);
+  return x < 0 ? nt : nt - div_bq<P2>(x, bq, bq_log2);
 }
 
 // Locate query tile `g` of one kv head in longest-first order: tiles sorted
@@ -361,15 +365,18 @@ __device__ __forceinline__ int tiles_with_work(int w, int lq, int lk, int bq, in
 // the tile in it. One wave runs this; returns false when g is past the last
 // tile. (my_lq, my_lk): sequence `lane`'s counts (the first 64 sequences;
 // further ones are read from memory).
+template <bool P2>
 __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
                                               const int32_t* __restrict__ seq_lens,
                                               int num_seqs, int total_q, int max_lk, int bq,
                                               int bq_log2, int causal, int g, int lane, int my_lq,
                                               int my_lk, int narrow_q, int& seq, int& q0) {
-  auto meta = [&](int s0, int& lq, int& lk) {
+  const int my_nt = my_lq > 0 ? div_bq<P2>(my_lq + bq - 1, bq, bq_log2) : 0;
+  auto meta = [&](int s0, int& lq, int& lk, int& nt) {
     if (s0 == 0) {
       lq = my_lq;
       lk = my_lk;
+      nt = my_nt;
       return;
     }
     const int s = s0 + lane;
@@ -381,21 +388,22 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
       if (lq <= narrow_q) lq = 0;   // taken by the narrow path
       lk = max(0, min(seq_lens[s], max_lk));
     }
+    nt = lq > 0 ? div_bq<P2>(lq + bq - 1, bq, bq_log2) : 0;
   };
   auto count = [&](int w) {   // tiles needing at least w key tiles
-    int c = 0;
-    for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
-      int lq, lk;
-      meta(s0, lq, lk);
-      c += tiles_with_work(w, lq, lk, bq, bq_log2, causal);
+    int c = tiles_with_work<P2>(w, my_nt, my_lq, my_lk, bq, bq_log2, causal);
+    for (int s0 = kWave; s0 < num_seqs; s0 += kWave) {
+      int lq, lk, nt;
+      meta(s0, lq, lk, nt);
+      c += tiles_with_work<P2>(w, nt, lq, lk, bq, bq_log2, causal);
     }
     return wave_sum_i(c);
   };
   if (g >= count(0)) return false;
-  int wmax = 0;
-  for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
-    int lq, lk;
-    meta(s0, lq, lk);
+  int wmax = (my_lk + kVlBN - 1) / kVlBN;
+  for (int s0 = kWave; s0 < num_seqs; s0 += kWave) {
+    int lq, lk, nt;
+    meta(s0, lq, lk, nt);
     wmax = max(wmax, (lk + kVlBN - 1) / kVlBN);
   }
   wmax = wave_max_i(wmax);
@@ -407,17 +415,16 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
   }
   int r = g - count(lo + 1);   // rank among the tiles needing exactly lo key tiles
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
-    int lq, lk;
-    meta(s0, lq, lk);
-    const int ge = tiles_with_work(lo, lq, lk, bq, bq_log2, causal);
-    const int c = ge - tiles_with_work(lo + 1, lq, lk, bq, bq_log2, causal);
+    int lq, lk, nt;
+    meta(s0, lq, lk, nt);
+    const int ge = tiles_with_work<P2>(lo, nt, lq, lk, bq, bq_log2, causal);
+    const int c = ge - tiles_with_work<P2>(lo + 1, nt, lq, lk, bq, bq_log2, causal);
     const int incl = wave_incl_scan_i(c);
     const int total = lane_value(incl, kWave - 1);
     if (r < total) {
       const unsigned long long hit = __ballot(incl - c <= r && r < incl);
       const int L = __builtin_ctzll(hit);
-      const int nt = div_bq(lane_value(lq, L) + bq - 1, bq, bq_log2);
-      const int t = nt - lane_value(ge, L) + (r - lane_value(incl - c, L));
+      const int t = lane_value(nt, L) - lane_value(ge, L) + (r - lane_value(incl - c, L));
       seq = s0 + L;
       q0 = t * bq;
       return true;
@@ -540,23 +547,29 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
       if (my_lq <= narrow_q) my_lq = 0;   // taken by the narrow path
       my_lk = max(0, min(seq_lens[lane], max_blocks_per_seq << log2_bs));
     }
-    const int nt0 = my_lq > 0 ? div_bq(my_lq + bq - 1, bq, bq_log2) : 0;
+    // tile count of sequence `lane` (the windowed and split lookups only)
+    auto lane_tiles = [&]() { return my_lq > 0 ? (my_lq + bq - 1) / bq : 0; };
     int seq = -1, q0 = 0, r0 = 0, lq_ = 0, lk_ = 0;
     // longest-first order; under a window a tile's key count is not
     // monotone in its position, so those tiles go by rank from the end
     bool found;
     if (SPLIT && extra) {   // the last tile of sequence xseq
-      const int ntx = xseq < kWave ? lane_value(nt0, xseq)
+      const int ntx = xseq < kWave ? lane_value(lane_tiles(), xseq)
                                    : seq_tiles(cu_seqlens_q, num_seqs, bq, total_q, xseq);
       found = ntx > 0;
       seq = xseq;
       q0 = (ntx - 1) * bq;
     } else {
-      found = (EXT && window_left >= 0)
-                  ? find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, nt0, seq, q0)
-                  : find_tile_lpt(cu_seqlens_q, seq_lens, num_seqs, total_q,
-                                  max_blocks_per_seq << log2_bs, bq, bq_log2, causal, tile, lane,
-                                  my_lq, my_lk, narrow_q, seq, q0);
+      if (EXT && window_left >= 0)
+        found = find_tile(cu_seqlens_q, num_seqs, bq, total_q, tile, lane, lane_tiles(), seq, q0);
+      else if (bq_log2 >= 0)   // uniform
+        found = find_tile_lpt<true>(cu_seqlens_q, seq_lens, num_seqs, total_q,
+                                    max_blocks_per_seq << log2_bs, bq, bq_log2, causal, tile,
+                                    lane, my_lq, my_lk, narrow_q, seq, q0);
+      else
+        found = find_tile_lpt<false>(cu_seqlens_q, seq_lens, num_seqs, total_q,
+                                     max_blocks_per_seq << log2_bs, bq, bq_log2, causal, tile,
+                                     lane, my_lq, my_lk, narrow_q, seq, q0);
     }
     if (!found) seq = -1;
     if (seq >= 0 && seq < kWave) {
