@@ -598,12 +598,13 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
   // rows of this lane: r = wave*32 + mt*16 + l16 -> (query i = r / group, head r % group)
   int q_pos[2], head[2], lim[2];
   bool row_ok[2];
-  // (shifts when the group size is a power of two, the usual case)
-  const int group_log2 = (group & (group - 1)) == 0 ? __builtin_ctz(group) : -1;
+  // r / group for r < 128 as (r * ceil(2^16 / group)) >> 16: exact, since
+  // the reciprocal's excess (< group <= 128) times r stays below 2^16
+  const int group_inv16 = (65536 + group - 1) / group;   // uniform
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int r = wave * kVlRowsWave + mt * 16 + l16;
-    const int i = group_log2 >= 0 ? r >> group_log2 : r / group;
+    const int i = (r * group_inv16) >> 16;
     q_pos[mt] = q0 + i;
     head[mt] = kvh * group + (r - i * group);
     row_ok[mt] = (i < bq) && (q_pos[mt] < lq);
