@@ -399,7 +399,8 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     }
     return wave_sum_i(c);
   };
-  if (g >= count(0)) return false;
+  // (no test of g against count(0): a g past the last tile ends the search
+  // below with lo = 0 and is not found by the scan)
   int wmax = (my_lk + kVlBN - 1) / kVlBN;
   for (int s0 = kWave; s0 < num_seqs; s0 += kWave) {
     int lq, lk, nt;
@@ -407,13 +408,20 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ cu,
     wmax = max(wmax, (lk + kVlBN - 1) / kVlBN);
   }
   wmax = wave_max_i(wmax);
-  int lo = 0, hi = wmax + 1;   // count(lo) > g >= count(hi)
+  // count(lo) > g >= count(hi) (for lo >= 1); c_hi = count(hi), which is 0
+  // past the longest key loop
+  int lo = 0, hi = wmax + 1, c_hi = 0;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (count(mid) > g) lo = mid;
-    else hi = mid;
+    const int c = count(mid);
+    if (c > g) {
+      lo = mid;
+    } else {
+      hi = mid;
+      c_hi = c;
+    }
   }
-  int r = g - count(lo + 1);   // rank among the tiles needing exactly lo key tiles
+  int r = g - c_hi;   // rank among the tiles needing exactly lo key tiles
   for (int s0 = 0; s0 < num_seqs; s0 += kWave) {
     int lq, lk, nt;
     meta(s0, lq, lk, nt);
