@@ -85,6 +85,22 @@ def test_varlen_many_sequences_ragged_queries(causal):
     check_varlen(case)
 
 
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (12, 2)])
+def test_varlen_many_sequences_odd_groups(hq, hkv):
+    """More than 64 sequences with a group of 3 or 6 query heads per kv head:
+    query tiles of 42 or 21 positions (not a power of two), so the
+    longest-first tile lookup takes its division path, also for the
+    sequences past the first 64 that it reads from memory."""
+    rng = np.random.default_rng(13 + hq)
+    ql = rng.integers(0, 90, size=100)
+    kl = ql + rng.integers(0, 200, size=100)
+    ql[[0, 63, 64, 99]] = 0
+    ql[[2, 80]] = 1
+    case = wl.varlen_case(720 + hq, ql.tolist(), kl.tolist(), hq, hkv, 128, 32, "bf16",
+                          causal=True)
+    check_varlen(case)
+
+
 def test_packed_prefill_named_workload():
     """16 sequences, lengths log-uniform in [64, 2048], 32/8 heads, bs 128:
     every query row of every head checked."""
