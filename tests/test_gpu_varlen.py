@@ -101,6 +101,20 @@ def test_varlen_many_sequences_odd_groups(hq, hkv):
     check_varlen(case)
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(64, 1, 64), (71, 1, 128), (128, 1, 64), (40, 2, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_wide_groups(hq, hkv, d, causal):
+    """Groups of 64, 71, 128 and 20 query heads per kv head: query tiles of
+    2, 1, 1 and 6 positions (71 and 20 leave padding rows in every tile),
+    so no sequence takes the narrow path and every query is a tile of its
+    own or shares one with a few neighbours; Lq < Lk, Lq = Lk, Lq > Lk and
+    an empty context."""
+    ql = [1, 5, 33, 70, 3, 9]
+    kl = [40, 5, 100, 70, 0, 2]
+    case = wl.varlen_case(740 + hq + d + causal, ql, kl, hq, hkv, d, 16, "bf16", causal=causal)
+    check_varlen(case)
+
+
 def test_packed_prefill_named_workload():
     """16 sequences, lengths log-uniform in [64, 2048], 32/8 heads, bs 128:
     every query row of every head checked."""
