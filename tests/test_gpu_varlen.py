@@ -115,6 +115,22 @@ def test_varlen_wide_groups(hq, hkv, d, causal):
     check_varlen(case)
 
 
+def test_varlen_large_batch_sampled():
+    """31578 packed queries (8 sequences up to 8192 tokens, 32/8 heads,
+    bs 16): ~7900 query-tile workgroups and key loops of up to 128
+    tiles. Sampled (row, head) pairs: each sequence's first and last rows
+    on every head, and 600 random pairs."""
+    lens = [4096, 8192, 4001, 3000, 4096, 1, 4096, 4096]
+    case = wl.varlen_case(760, lens, lens, 32, 8, 128, 16, "bf16", causal=True)
+    rng = np.random.default_rng(761)
+    cu = case.cu_seqlens_q
+    rows = [(int(r), h) for b in range(len(lens)) for r in {cu[b], cu[b + 1] - 1}
+            for h in range(32)]
+    rows += [(int(r), int(h)) for r, h in zip(rng.integers(0, cu[-1], 600),
+                                              rng.integers(0, 32, 600))]
+    check_varlen(case, rows=rows)
+
+
 def test_packed_prefill_named_workload():
     """16 sequences, lengths log-uniform in [64, 2048], 32/8 heads, bs 128:
     every query row of every head checked."""
