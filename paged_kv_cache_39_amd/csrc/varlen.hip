@@ -236,33 +236,43 @@ __device__ __forceinline__ void varlen_narrow(
   for (int nd = 0; nd < ND; ++nd)
     *reinterpret_cast<f32x4_t*>(s_o + (wave * 16 + l16) * N::oRow + 16 * nd + 4 * g4) = acc[nd];
   __syncthreads();
+  // a thread merges 8 consecutive dims of a row: one 16-byte store of the
+  // output (two of the fp32 chunk output)
+  constexpr int TPR = D / 8;   // threads per row
   const int rows = lq * group;
-  for (int idx = tid; idx < rows * D; idx += kVlThreads) {
-    const int r = idx / D, d = idx - r * D;
+  for (int idx = tid; idx < rows * TPR; idx += kVlThreads) {
+    const int r = idx / TPR, d0 = (idx - r * TPR) * 8;
     float mm = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kVlWaves; ++w) mm = fmaxf(mm, s_ml[(w * 16 + r) * 2]);
     const float mr = safe_max_ref(mm);
-    float ll = 0.f, a = 0.f;
+    float ll = 0.f;
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kVlWaves; ++w) {
       const float wt = fast_exp2(s_ml[(w * 16 + r) * 2] - mr);
       ll += s_ml[(w * 16 + r) * 2 + 1] * wt;
-      a += s_o[(w * 16 + r) * N::oRow + d] * wt;
+      const float* so = s_o + (w * 16 + r) * N::oRow + d0;
+      a0 += *reinterpret_cast<const f32x4_t*>(so) * wt;
+      a1 += *reinterpret_cast<const f32x4_t*>(so + 4) * wt;
     }
     if (ws_row0 >= 0) {
       // a chunk of a cut sequence: (max, sum, output) relative to 2^max for
       // the merge kernel, row r at slot ws_row0 + r
       const int64_t slot_i = ws_row0 + r;
-      ws_o[slot_i * D + d] = a;
-      if (d == 0) {
+      *reinterpret_cast<f32x4_t*>(ws_o + slot_i * D + d0) = a0;
+      *reinterpret_cast<f32x4_t*>(ws_o + slot_i * D + d0 + 4) = a1;
+      if (d0 == 0) {
         ws_ml[slot_i * 2 + 0] = mm;
         ws_ml[slot_i * 2 + 1] = ll;
       }
     } else {
       const int i = r / group;
-      out[((size_t)(r0 + i) * num_q_heads + kvh * group + (r - i * group)) * D + d] =
-          from_f32<Ty>(ll > 0.f ? a / ll : 0.f);
+      const float inv = ll > 0.f ? 1.f / ll : 0.f;
+      *reinterpret_cast<u32x4_t*>(out + ((size_t)(r0 + i) * num_q_heads + kvh * group +
+                                         (r - i * group)) * D + d0) =
+          u32x4_t{Mma<Ty>::pack(a0[0] * inv, a0[1] * inv), Mma<Ty>::pack(a0[2] * inv, a0[3] * inv),
+                  Mma<Ty>::pack(a1[0] * inv, a1[1] * inv), Mma<Ty>::pack(a1[2] * inv, a1[3] * inv)};
     }
   }
 }
@@ -1010,18 +1020,31 @@ __global__ __launch_bounds__(kVlThreads, 2) void varlen_prefill_kernel(
     return;
   }
   // ---- normalise and store: lane holds O^T[16nd + 4*g4 + i][row] ----
+  // Each pair of 16-dim tiles (2p, 2p+1) is exchanged between the lane
+  // groups g4 and g4 ^ 1 (v_permlane16_swap swaps the odd 16-lane rows of
+  // its first operand with the even rows of its second), after which group
+  // g4 holds the 8 consecutive dims 32p + 8 * (g4 with its two bits
+  // swapped) .. + 7 of its row: a row's 64 bytes of the pair go out as one
+  // 16-byte store from each of its four lanes (half the store instructions
+  // of 8-byte stores of each tile).
+  const int g4s = ((g4 & 1) << 1) | (g4 >> 1);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const float lt = lacc[mt][0];
-    if (!row_ok[mt]) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* dst = out + ((size_t)(row0 + q_pos[mt]) * num_q_heads + head[mt]) * D + 4 * g4;
+    uint16_t* dst = out + ((size_t)(row0 + q_pos[mt]) * num_q_heads + head[mt]) * D + 8 * g4s;
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd) {
-      u32x2_t w;
-      w[0] = Mma<Ty>::pack(acc[mt][nd][0] * inv, acc[mt][nd][1] * inv);
-      w[1] = Mma<Ty>::pack(acc[mt][nd][2] * inv, acc[mt][nd][3] * inv);
-      *reinterpret_cast<u32x2_t*>(dst + 16 * nd) = w;
+    for (int p = 0; p < ND / 2; ++p) {
+      const f32x4_t& a = acc[mt][2 * p];
+      const f32x4_t& c = acc[mt][2 * p + 1];
+      const auto s0 = __builtin_amdgcn_permlane16_swap(Mma<Ty>::pack(a[0] * inv, a[1] * inv),
+                                                       Mma<Ty>::pack(c[0] * inv, c[1] * inv),
+                                                       false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(Mma<Ty>::pack(a[2] * inv, a[3] * inv),
+                                                       Mma<Ty>::pack(c[2] * inv, c[3] * inv),
+                                                       false, false);
+      if (row_ok[mt])
+        *reinterpret_cast<u32x4_t*>(dst + 32 * p) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
     }
   }
 }
