@@ -15,7 +15,10 @@
  * --------------------------------
  *  - Tensor arguments are DEVICE pointers owned by the caller. The library
  *    never frees, retains or allocates memory.
- *  - All tensors are dense, row-major (C order), with no padding.
+ *  - All tensors are dense, row-major (C order), with no padding. Tensor
+ *    data pointers (queries, outputs, keys / values, the pool) are 16-byte
+ *    aligned, as device allocations are: the kernels move 16-byte pieces.
+ *    A call given one that is not returns PKV_ERR_UNSUPPORTED.
  *  - Pool layout (k_cache and v_cache alike): [num_blocks, block_size,
  *    num_kv_heads, head_dim]. Slot s is row s of the pool viewed as
  *    [num_blocks * block_size, num_kv_heads * head_dim].
@@ -62,7 +65,8 @@ typedef enum {
   PKV_ERR_NULL = -1,        /* a required pointer is NULL */
   PKV_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
   PKV_ERR_DTYPE = -3,       /* dtype code unknown or not accepted by this call */
-  PKV_ERR_UNSUPPORTED = -4, /* head_dim / block_size outside the supported set */
+  PKV_ERR_UNSUPPORTED = -4, /* head_dim / block_size / GQA group outside the supported
+                               set, or a tensor pointer not 16-byte aligned */
   PKV_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
   PKV_ERR_HIP = -6,         /* the HIP runtime rejected a launch */
   PKV_ERR_NO_BLOCKS = -7,   /* block manager: not enough free blocks */

@@ -4,6 +4,7 @@
 // Every check here runs before any HIP call, so an invalid call returns its
 // status without touching the device (and works on a machine with no GPU).
 
+#include <initializer_list>
 #include <limits.h>
 
 #include <atomic>
@@ -52,6 +53,15 @@ int check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (num_blocks > (int64_t)INT32_MAX / block_size) return PKV_ERR_SHAPE;
   return PKV_OK;
+}
+
+// The kernels move tensor data (queries, outputs, new rows, the pool) in
+// 16-byte pieces: every such pointer must be 16-byte aligned, as every
+// device allocator's blocks are.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
+  return true;
 }
 
 int decode_num_parts(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
@@ -143,6 +153,7 @@ static int write_decode_impl(void* out, const void* q, void* k_cache, void* v_ca
   if (!out || !q || !k_cache || !v_cache || !key || !value || !slot_mapping || !block_table ||
       !context_lens)
     return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache, key, value})) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
                                                             max_blocks_per_seq, block_size);
   if (noalloc) {
@@ -205,6 +216,7 @@ static int varlen_impl(void* out, const void* q, const int32_t* cu_seqlens_q,
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !seq_lens)
     return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PKV_ERR_UNSUPPORTED;
   // the one-dimensional grid: (query tiles [+ split chunk slots]) x kv heads
   const int64_t splits =
       split ? pkv::plan_varlen_split(max_blocks_per_seq, block_size).max_splits : 1;
@@ -260,7 +272,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_NULL: return "a required pointer is NULL";
     case PKV_ERR_SHAPE: return "a size is out of range or inconsistent";
     case PKV_ERR_DTYPE: return "dtype code unknown or not accepted by this call";
-    case PKV_ERR_UNSUPPORTED: return "head_dim or block_size outside the supported set";
+    case PKV_ERR_UNSUPPORTED: return "head_dim, block_size or GQA group outside the supported set, or a tensor pointer not 16-byte aligned";
     case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
     case PKV_ERR_HIP: return "the HIP runtime rejected a launch";
     case PKV_ERR_NO_BLOCKS: return "not enough free cache blocks";
@@ -314,6 +326,7 @@ int paged_kv_write(void* k_cache, void* v_cache, const void* key, const void* va
   if (st != PKV_OK) return st;
   if (num_tokens == 0) return PKV_OK;
   if (!k_cache || !v_cache || !key || !value || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16({k_cache, v_cache, key, value})) return PKV_ERR_UNSUPPORTED;
   const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
   if (row_bytes > INT32_MAX / 2) return PKV_ERR_SHAPE;
   if (num_tokens > INT64_MAX / (row_bytes / 16)) return PKV_ERR_SHAPE;
@@ -353,6 +366,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_cache, const 
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
                                                             max_blocks_per_seq, block_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
@@ -474,6 +488,7 @@ int paged_attention_decode_ex(void* out, const void* q, const void* k_cache, con
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
                                                             max_blocks_per_seq, block_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
@@ -512,6 +527,7 @@ int paged_kv_write_int8(void* k_cache, void* v_cache, const void* key, const voi
   if (num_tokens == 0) return PKV_OK;
   if (!k_cache || !v_cache || !key || !value || !k_scale || !v_scale || !slot_mapping)
     return PKV_ERR_NULL;
+  if (!aligned16({k_cache, v_cache, key, value})) return PKV_ERR_UNSUPPORTED;
   const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
   if (row_elems * 4 > INT32_MAX / 2) return PKV_ERR_SHAPE;
   if (num_tokens > INT64_MAX / (row_elems / 16)) return PKV_ERR_SHAPE;
@@ -540,6 +556,7 @@ int paged_attention_decode_int8(void* out, const void* q, const void* k_cache, c
   if (!out || !q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table ||
       !context_lens)
     return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
                                                             max_blocks_per_seq, block_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
@@ -586,6 +603,7 @@ int paged_kv_write_decode_int8(void* out, const void* q, void* k_cache, void* v_
   if (!out || !q || !k_cache || !v_cache || !key || !value || !k_scale || !v_scale ||
       !slot_mapping || !block_table || !context_lens)
     return PKV_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache, key, value})) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, head_dim,
                                                             max_blocks_per_seq, block_size);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
@@ -627,6 +645,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
   if (st != PKV_OK) return st;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_ERR_NULL;
+  if (!aligned16({k_cache, v_cache})) return PKV_ERR_UNSUPPORTED;
   const int eb = dtype == PKV_I8 ? 1 : elem_bytes(dtype);
   const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * eb;
   if (block_bytes / 16 > INT32_MAX) return PKV_ERR_SHAPE;

@@ -249,6 +249,17 @@ def varlen(L, **kw):
                                     a["bs"], a["maxblk"], a["nb"], a["dtype"], None)
 
 
+def test_misaligned_tensor_pointer(L):
+    """A tensor pointer off a 16-byte boundary is refused before any launch
+    (the workspace check that follows it would refuse these calls too, so
+    nothing here can reach a kernel)."""
+    off = ctypes.c_void_p(0x1000 + 8)
+    assert decode(L, wsb=0) == PKV_ERR_WORKSPACE
+    for arg in ("out", "q", "k", "v"):
+        assert decode(L, wsb=0, **{arg: off}) == PKV_ERR_UNSUPPORTED
+    assert decode(L, wsb=0, bt=ctypes.c_void_p(0x1000 + 4)) == PKV_ERR_WORKSPACE  # int32 metadata
+
+
 def test_varlen_validation(L):
     assert varlen(L, dtype=0) == PKV_ERR_DTYPE                 # fp32 not on the matrix-core path
     assert varlen(L, dtype=9) == PKV_ERR_DTYPE
